@@ -1,0 +1,221 @@
+// api.cpp -- the C ABI declared in include/oproj.h: host-side validation and
+// dispatch to the gfx950 kernels.  Nothing here allocates or synchronises.
+#include "oproj.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Head geometry and shape checks shared by every entry point.  Mirrors the
+// preconditions fused_inv_rope_fp8_quant asserts (vLLM API page
+// "vllm.models.deepseek_v4.common.ops.fused_inv_rope_fp8_quant"): H = G*hpg,
+// head_dim = nope + rope, head_dim % block == 0, nope % block == block - rope,
+// rope even; the fixed geometry of this library is 448 + 64 with blocks of 128.
+oproj_status check_shape(const oproj_shape* s, bool need_rank) {
+    if (!s) return OPROJ_E_NULL;
+    if (s->T < 0 || s->n_groups < 1 || s->heads_per_group < 1 || s->max_pos < 1)
+        return OPROJ_E_SHAPE;
+    if (s->nope_dim < 0 || s->rope_dim < 0 || s->quant_block < 1) return OPROJ_E_SHAPE;
+    const int64_t hd = s->nope_dim + s->rope_dim;
+    if (hd % s->quant_block != 0) return OPROJ_E_SHAPE;
+    if (s->nope_dim % s->quant_block != s->quant_block - s->rope_dim) return OPROJ_E_SHAPE;
+    if (s->rope_dim % 2 != 0) return OPROJ_E_SHAPE;
+    if (s->nope_dim != 448 || s->rope_dim != 64 || s->quant_block != 128) return OPROJ_E_MODE;
+    const int64_t hpg = s->heads_per_group;
+    if (!(hpg == 1 || hpg == 2 || hpg == 4 || hpg % 8 == 0)) return OPROJ_E_MODE;
+    if (s->T > (int64_t(1) << 31) || s->n_groups * hpg > 65536) return OPROJ_E_SHAPE;
+    if (need_rank && (s->o_lora_rank < 64 || s->o_lora_rank % 64 != 0 || s->o_lora_rank > 65536))
+        return OPROJ_E_SHAPE;
+    return OPROJ_OK;
+}
+
+oproj::ActLayout default_layout(const oproj_shape* s) {
+    const int64_t D = s->heads_per_group * 512, KB = D / 128;
+    oproj::ActLayout l;
+    l.stride_t = D;
+    l.stride_g = s->T * D;
+    l.s_stride_t = 1;
+    l.s_stride_kb = s->T;
+    l.s_stride_g = KB * s->T;
+    return l;
+}
+
+oproj_status check_layout(const oproj_act_layout* l) {
+    if (!l) return OPROJ_OK;
+    if (l->stride_t < 0 || l->stride_g < 0 || l->s_stride_t < 0 || l->s_stride_g < 0 ||
+        l->s_stride_kb < 0)
+        return OPROJ_E_SHAPE;
+    if (l->stride_t % 16 != 0 || l->stride_g % 16 != 0) return OPROJ_E_ALIGN;
+    return OPROJ_OK;
+}
+
+oproj::ActLayout to_layout(const oproj_act_layout* l, const oproj_shape* s) {
+    if (!l) return default_layout(s);
+    oproj::ActLayout o;
+    o.stride_t = l->stride_t;
+    o.stride_g = l->stride_g;
+    o.s_stride_t = l->s_stride_t;
+    o.s_stride_g = l->s_stride_g;
+    o.s_stride_kb = l->s_stride_kb;
+    return o;
+}
+
+oproj_status from_hip(hipError_t e) { return e == hipSuccess ? OPROJ_OK : OPROJ_E_HIP; }
+
+size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* oproj_status_string(oproj_status s) {
+    switch (s) {
+        case OPROJ_OK: return "ok";
+        case OPROJ_E_NULL: return "null pointer";
+        case OPROJ_E_SHAPE: return "invalid shape";
+        case OPROJ_E_ALIGN: return "misaligned pointer or stride";
+        case OPROJ_E_MODE: return "unsupported mode or head geometry";
+        case OPROJ_E_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+const char* oproj_version(void) { return "0.1.0"; }
+
+oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                                  const int64_t* positions, const float* cos_sin, void* a_codes,
+                                  float* a_scales, const oproj_act_layout* out_layout,
+                                  void* stream) {
+    oproj_status st = check_shape(shape, false);
+    if (st != OPROJ_OK) return st;
+    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if ((st = check_layout(out_layout)) != OPROJ_OK) return st;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!o || !positions || !cos_sin || !a_codes || !a_scales) return OPROJ_E_NULL;
+    if (!aligned16(o) || !aligned16(cos_sin) || !aligned16(a_codes) ||
+        (reinterpret_cast<uintptr_t>(positions) & 7u) || (reinterpret_cast<uintptr_t>(a_scales) & 3u))
+        return OPROJ_E_ALIGN;
+    oproj::RopeQuantArgs a;
+    a.T = shape->T;
+    a.G = shape->n_groups;
+    a.hpg = shape->heads_per_group;
+    a.max_pos = shape->max_pos;
+    a.pow2 = scale_mode == OPROJ_SCALE_POW2;
+    a.o = static_cast<const uint16_t*>(o);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.codes = static_cast<uint8_t*>(a_codes);
+    a.scales = a_scales;
+    a.lay = to_layout(out_layout, shape);
+    return from_hip(oproj::launch_inv_rope_quant(a, static_cast<hipStream_t>(stream)));
+}
+
+oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
+                                const float* a_scales, const oproj_act_layout* a_layout,
+                                const void* w_codes, const float* w_scales, int32_t w_block,
+                                void* z, void* stream) {
+    oproj_status st = check_shape(shape, true);
+    if (st != OPROJ_OK) return st;
+    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
+    if ((st = check_layout(a_layout)) != OPROJ_OK) return st;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!a_codes || !a_scales || !w_codes || !w_scales || !z) return OPROJ_E_NULL;
+    if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(z) ||
+        (reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scales) & 3u))
+        return OPROJ_E_ALIGN;
+    oproj::GroupedGemmArgs a;
+    a.T = shape->T;
+    a.G = shape->n_groups;
+    a.D = shape->heads_per_group * 512;
+    a.R = shape->o_lora_rank;
+    a.mx = scale_mode == OPROJ_SCALE_POW2;
+    a.w_1x128 = w_block == OPROJ_WBLOCK_1x128;
+    a.a = static_cast<const uint8_t*>(a_codes);
+    a.sa = a_scales;
+    a.lay = to_layout(a_layout, shape);
+    a.w = static_cast<const uint8_t*>(w_codes);
+    a.sw = w_scales;
+    a.z = static_cast<uint16_t*>(z);
+    return from_hip(oproj::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                                   void* y, void* stream) {
+    if (M < 0 || N < 1 || K < 64 || K % 64 != 0 || N % 16 != 0) return OPROJ_E_SHAPE;
+    if (M == 0) return OPROJ_OK;
+    if (!x || !w || !y) return OPROJ_E_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return OPROJ_E_ALIGN;
+    oproj::DenseGemmArgs a;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w);
+    a.y = static_cast<uint16_t*>(y);
+    return from_hip(oproj::launch_dense_bf16_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden) {
+    if (check_shape(shape, true) != OPROJ_OK) return 0;
+    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;
+    const size_t D = (size_t)shape->heads_per_group * 512, KB = D / 128;
+    size_t b = round_up(T * G * D) + round_up(T * G * KB * sizeof(float));
+    if (hidden > 0) b += round_up(T * G * (size_t)shape->o_lora_rank * 2);
+    return b;
+}
+
+oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                         const int64_t* positions, const float* cos_sin, const void* w_codes,
+                         const float* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
+                         void* workspace, size_t workspace_bytes, void* out, void* stream) {
+    oproj_status st = check_shape(shape, true);
+    if (st != OPROJ_OK) return st;
+    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
+    if (wo_b && (hidden < 16 || hidden % 16 != 0)) return OPROJ_E_SHAPE;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!o || !positions || !cos_sin || !w_codes || !w_scales || !workspace || !out)
+        return OPROJ_E_NULL;
+    if (workspace_bytes < oproj_fused_workspace_bytes(shape, wo_b ? hidden : 0)) return OPROJ_E_SHAPE;
+    if (!aligned16(workspace)) return OPROJ_E_ALIGN;
+    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;
+    const size_t D = (size_t)shape->heads_per_group * 512, KB = D / 128;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* codes = ws;
+    float* scales = reinterpret_cast<float*>(ws + round_up(T * G * D));
+    void* zbuf = wo_b ? (void*)(ws + round_up(T * G * D) + round_up(T * G * KB * sizeof(float))) : out;
+    st = oproj_inv_rope_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, stream);
+    if (st != OPROJ_OK) return st;
+    st = oproj_grouped_wo_a(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block,
+                            zbuf, stream);
+    if (st != OPROJ_OK || !wo_b) return st;
+    return oproj_dense_bf16_gemm(shape->T, hidden, shape->n_groups * shape->o_lora_rank, zbuf, wo_b,
+                                 out, stream);
+}
+
+oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
+                                   const float* w, void* codes, float* scales, void* stream) {
+    if (rows < 0 || K < 128 || K % 128 != 0) return OPROJ_E_SHAPE;
+    if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
+    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (rows == 0) return OPROJ_OK;
+    if (!w || !codes || !scales) return OPROJ_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+        return OPROJ_E_ALIGN;
+    oproj::WeightQuantArgs a;
+    a.rows = rows;
+    a.K = K;
+    a.brows = w_block == OPROJ_WBLOCK_1x128 ? 1 : 128;
+    a.pow2 = scale_mode == OPROJ_SCALE_POW2;
+    a.w = w;
+    a.codes = static_cast<uint8_t*>(codes);
+    a.scales = scales;
+    return from_hip(oproj::launch_quantize_weight(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public C ABI is include/oproj.h).  Arguments arrive validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oproj {
+
+struct ActLayout {
+    int64_t stride_t, stride_g;              // codes, bytes == elements
+    int64_t s_stride_t, s_stride_g, s_stride_kb;  // scales, floats
+};
+
+struct RopeQuantArgs {
+    int64_t T, G, hpg, max_pos;
+    int pow2;
+    const uint16_t* o;        // bf16 [T][G*hpg][512]
+    const int64_t* positions; // [T]
+    const float* cos_sin;     // [max_pos][64]
+    uint8_t* codes;
+    float* scales;
+    ActLayout lay;
+};
+hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t s);
+
+struct WeightQuantArgs {
+    int64_t rows, K, brows;
+    int pow2;
+    const float* w;
+    uint8_t* codes;
+    float* scales;
+};
+hipError_t launch_quantize_weight(const WeightQuantArgs& a, hipStream_t s);
+
+struct GroupedGemmArgs {
+    int64_t T, G, D, R;
+    int mx;        // both scale sets are powers of two: use block-scaled MFMA
+    int w_1x128;   // weight scales per row (else 128x128 tiles of the flat matrix)
+    const uint8_t* a;
+    const float* sa;
+    ActLayout lay;
+    const uint8_t* w;
+    const float* sw;
+    uint16_t* z;   // bf16 [T][G][R]
+};
+hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t s);
+
+struct DenseGemmArgs {
+    int64_t M, N, K;
+    const uint16_t* x;  // bf16 [M][K]
+    const uint16_t* w;  // bf16 [N][K]
+    uint16_t* y;        // bf16 [M][N]
+};
+hipError_t launch_dense_bf16_gemm(const DenseGemmArgs& a, hipStream_t s);
+
+}  // namespace oproj

@@ -1,0 +1,321 @@
+"""Benchmark of the O-projection front half on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+inverse RoPE + 1x128 FP8 quantisation (oproj_inv_rope_quant) followed by the
+grouped wo_a GEMM (oproj_grouped_wo_a) -- exactly what oproj_fused enqueues --
+plus the dense wo_b GEMM for the workload that has one.  The default workload
+is the decode batch (T=64, 16 groups x 8 heads, D=4096, R=1024).
+
+Inputs are resident in HBM before timing starts.  The steps rotate through
+several copies of the inputs, weights and workspaces (more bytes than the
+256 MB last-level cache) so weights are streamed from HBM every step.  The
+rotation of C steps is captured once in a HIP graph and replayed (a decode
+step is a few microseconds of GPU work, shorter than a Python launch).
+
+Printed: one JSON line with the throughput, the roofline of the dominant
+kernel (algorithmic bytes or FLOPs per launch / its average launch time from
+HIP events around back-to-back replays) and the oracle's CPU baseline on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0  # dense BF16 MFMA
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_bytes_quant(w) -> int:
+    """Algorithmic HBM bytes of a1+a2: read bf16 o, positions and the table
+    rows; write FP8 codes and fp32 scales."""
+    return w.T * w.H * 512 * 2 + w.T * 8 + w.T * 64 * 4 + w.T * w.n_groups * w.D + w.T * w.n_groups * w.KB * 4
+
+
+def kernel_bytes_gemm(w) -> int:
+    """Algorithmic HBM bytes of a3: FP8 weight + weight scales + live FP8
+    activations + activation scales + bf16 z."""
+    G, R, D, KB, T = w.n_groups, w.o_lora_rank, w.D, w.KB, w.T
+    wrows = G * R
+    wscales = (wrows if w.w_block_rows == 1 else (wrows + 127) // 128) * KB * 4
+    return wrows * D + wscales + T * G * D + T * G * KB * 4 + T * G * R * 2
+
+
+def kernel_flops_gemm(w) -> int:
+    return 2 * w.T * w.n_groups * w.o_lora_rank * w.D
+
+
+def source_sha(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "attention_output_projection_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha") != sha:
+        return None
+    return int(d["bytes_per_launch"])
+
+
+def cpu_baseline(w, o, pos, tab, wmat, max_tokens: int):
+    """The oracle as it stands, on the first tokens of the same batch."""
+    import oracle
+
+    S = min(w.T, max_tokens)
+    qw, sw = oracle.quant_weight(wmat, w.w_block_rows, w.pow2)  # offline weight prep, untimed
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    qa, sa = oracle.inv_rope_quant(o[:S], pos[:S], tab, w.n_groups, w.heads_per_group, pow2=w.pow2)
+    oracle.grouped_gemm(qa, sa, qw, sw, w.n_groups, w.o_lora_rank, w.w_block_rows)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of the {w.name} batch: inverse RoPE + quant + "
+                      f"grouped wo_a in fp64, {dt:.2f} s"}
+
+
+def main() -> int:
+    ap_ = argparse.ArgumentParser()
+    ap_.add_argument("--gpus", type=int, default=1)
+    ap_.add_argument("--steps", type=int, default=2000)
+    ap_.add_argument("--warmup", type=int, default=200)
+    ap_.add_argument("--workload", default="decode", choices=["decode", "prefill", "pow2", "full", "tiny"])
+    ap_.add_argument("--copies", type=int, default=0, help="input/weight copies rotated (0: auto)")
+    ap_.add_argument("--kernel-reps", type=int, default=50, help="graph replays per kernel timing")
+    ap_.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
+    ap_.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap_.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over tokens or groups, see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import attention_output_projection_amd as ap
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    ap.load_library()
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    log(f"workload {w.name}: T={w.T} G={w.n_groups} hpg={w.heads_per_group} D={w.D} R={w.o_lora_rank}")
+
+    # ---------------------------------------------------------------- inputs
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    wmat = wl.wo_a_f32(w)
+    wob = wl.wo_b_bf16(w) if w.hidden else None
+    per_copy = w.n_groups * w.o_lora_rank * w.D + o.nbytes + (wob.nbytes if wob is not None else 0)
+    copies = args.copies or max(2, min(16, int(np.ceil(768e6 / per_copy))))
+    log(f"{copies} rotating copies of {per_copy / 1e6:.1f} MB")
+
+    shp = ap.Shape(T=w.T, n_groups=w.n_groups, heads_per_group=w.heads_per_group,
+                   o_lora_rank=w.o_lora_rank, max_pos=w.max_pos)
+    mode = ap.OPROJ_SCALE_POW2 if w.pow2 else ap.OPROJ_SCALE_FP32
+    wblock = ap.OPROJ_WBLOCK_1x128 if w.w_block_rows == 1 else ap.OPROJ_WBLOCK_128x128
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    d_tab = t(tab)
+    d_pos = t(pos)
+    d_w32 = t(wmat)
+    wrows = w.n_groups * w.o_lora_rank
+    srows = wrows if w.w_block_rows == 1 else (wrows + 127) // 128
+    C = []
+    for i in range(copies):
+        c = {}
+        c["o"] = t(o.view(np.int16))
+        c["wq"] = torch.empty((wrows, w.D), dtype=torch.uint8, device=dev)
+        c["ws"] = torch.empty((srows, w.KB), dtype=torch.float32, device=dev)
+        ap.oproj_quantize_weight(wrows, w.D, wblock, mode, d_w32, c["wq"], c["ws"])
+        c["codes"] = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=dev)
+        c["scales"] = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=dev)
+        c["z"] = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=dev)
+        if wob is not None:
+            c["wob"] = t(wob.view(np.int16))
+            c["y"] = torch.empty((w.T, w.hidden), dtype=torch.int16, device=dev)
+        C.append(c)
+    del d_w32
+    torch.cuda.synchronize()
+
+    def quant(c):
+        ap.oproj_inv_rope_quant(shp, mode, c["o"], d_pos, d_tab, c["codes"], c["scales"])
+
+    def gemm(c):
+        ap.oproj_grouped_wo_a(shp, mode, c["codes"], c["scales"], None, c["wq"], c["ws"], wblock, c["z"])
+
+    def wo_b(c):
+        ap.oproj_dense_bf16_gemm(w.T, w.hidden, wrows, c["z"], c["wob"], c["y"])
+
+    def step(c):
+        quant(c)
+        gemm(c)
+        if wob is not None:
+            wo_b(c)
+
+    # eager reference result of copy 0
+    step(C[0])
+    torch.cuda.synchronize()
+    eager_out = (C[0]["y"] if wob is not None else C[0]["z"]).clone()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in C:  # one eager pass on the capture stream first
+                fn(c)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for c in C:
+                fn(c)
+        torch.cuda.synchronize()
+        return g
+
+    g_step = capture(step)
+    g_quant = capture(quant)
+    g_gemm = capture(gemm)
+    g_wob = capture(wo_b) if wob is not None else None
+
+    # replays must reproduce the eager result
+    for _ in range(3):
+        g_step.replay()
+        torch.cuda.synchronize()
+        out = C[0]["y"] if wob is not None else C[0]["z"]
+        if not torch.equal(out, eager_out):
+            log("graph replay differs from the eager result")
+            return 1
+        step(C[0])  # eager work between replays
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    reps = max(1, args.steps // copies)
+    K = reps * copies
+    wreps = max(1, args.warmup // copies)
+    for _ in range(wreps):
+        g_step.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(reps):
+        g_step.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    ms_per_step_ev = ev0.elapsed_time(ev1) / K
+    log(f"{K} steps: {ms_per_step * 1e3:.2f} us/step (host clock), {ms_per_step_ev * 1e3:.2f} us/step (events)")
+
+    # ---------------------------------------------------------------- per-kernel launch times
+    def kernel_time_us(g):
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.kernel_reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (args.kernel_reps * copies)
+
+    t_quant = kernel_time_us(g_quant)
+    t_gemm = kernel_time_us(g_gemm)
+    t_wob = kernel_time_us(g_wob) if g_wob is not None else None
+    log(f"kernel averages: quant {t_quant:.2f} us, grouped gemm {t_gemm:.2f} us"
+        + (f", wo_b {t_wob:.2f} us" if t_wob else ""))
+
+    kernels = {
+        "inv_rope_quant": {"us": t_quant, "bound": "hbm", "bytes": kernel_bytes_quant(w),
+                           "GB/s": kernel_bytes_quant(w) / (t_quant * 1e3)},
+        "grouped_wo_a": {"us": t_gemm, "bytes": kernel_bytes_gemm(w), "flops": kernel_flops_gemm(w),
+                         "GB/s": kernel_bytes_gemm(w) / (t_gemm * 1e3),
+                         "TFLOP/s": kernel_flops_gemm(w) / (t_gemm * 1e6)},
+    }
+    ai = kernel_flops_gemm(w) / kernel_bytes_gemm(w)
+    gemm_bound = "hbm" if ai < FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "mfma"
+    kernels["grouped_wo_a"]["bound"] = gemm_bound
+    if t_wob is not None:
+        fl = 2 * w.T * w.hidden * wrows
+        kernels["wo_b"] = {"us": t_wob, "bound": "mfma", "flops": fl, "TFLOP/s": fl / (t_wob * 1e6)}
+
+    dominant = max(kernels, key=lambda k: kernels[k]["us"])
+    kd = kernels[dominant]
+    if dominant == "inv_rope_quant":
+        sha = source_sha("rope_quant.hip", "device_common.hpp")
+        achieved, peak, unit, bound = kd["GB/s"], HBM_PEAK_GBS, "GB/s", "hbm"
+    elif dominant == "grouped_wo_a":
+        sha = source_sha("gemm_fp8.hip", "device_common.hpp")
+        if gemm_bound == "hbm":
+            achieved, peak, unit, bound = kd["GB/s"], HBM_PEAK_GBS, "GB/s", "hbm"
+        else:
+            achieved, peak, unit, bound = kd["TFLOP/s"], FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        sha = source_sha("gemm_bf16.hip", "device_common.hpp")
+        achieved, peak, unit, bound = kd["TFLOP/s"], BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    traffic = load_traffic(dominant, w.name, sha)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        cpu = cpu_baseline(w, o, pos, tab, wmat, args.cpu_tokens)
+        log(f"oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    tokens_per_s = w.T / (ms_per_step * 1e-3)
+    gemm_tflops = kernel_flops_gemm(w) / (ms_per_step * 1e9)
+    result = {
+        "metric": "tokens/s of inverse RoPE + FP8 quant + grouped wo_a"
+                  + (" + wo_b" if wob is not None else ""),
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": wreps * copies,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic (seeded SplitMix64 normals; random-init weights)",
+        "config": {"workload": f"{w.name}: T={w.T} n_groups={w.n_groups} heads_per_group={w.heads_per_group} "
+                               f"head_dim=512 D={w.D} o_lora_rank={w.o_lora_rank} max_pos={w.max_pos}"
+                               + (f" hidden={w.hidden}" if w.hidden else "")
+                               + f" scales={'pow2' if w.pow2 else 'fp32'}",
+                   "global_batch": w.T, "parallelism": "single GPU",
+                   "step_TFLOP/s": gemm_tflops, "copies_rotated": copies},
+        "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

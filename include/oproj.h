@@ -1,0 +1,178 @@
+/*
+ * oproj.h -- C ABI of the MI355X (gfx950) O-projection front half:
+ *   inverse RoPE -> 1x128 block FP8 e4m3fn quantisation -> grouped wo_a GEMM
+ *   [-> dense wo_b GEMM].
+ *
+ * Sources (web pages; cited by page title and section):
+ *  [FUSED] vLLM API page "vllm.models.deepseek_v4.common.ops.fused_inv_rope_fp8_quant",
+ *          fused_inv_rope_fp8_quant: parameters, returns and preconditions.
+ *  [OPROJ] vLLM API page "vllm.models.deepseek_v4.nvidia.ops.o_proj":
+ *          compute_fp8_einsum_recipe (scale recipes), deep_gemm_fp8_o_proj
+ *          (the path; caller-allocated z; pre-quantised input with padding groups).
+ *  [GWA]   vLLM API page "vllm.models.deepseek_v4.common.grouped_wo_a",
+ *          DeepseekV4GroupedWoA (group g meets only rows g*R .. g*R+R-1).
+ *  [SGL]   sglang source page "python/sglang/srt/models/deepseek_v4.py":
+ *          MQALayer.forward (inverse RoPE, group view, FP8 einsum, wo_b),
+ *          _dequant_fp8 (weight scales multiply), _setup_fp8_wo_a_scales.
+ *
+ * Conventions for every entry point
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates device memory, never synchronises the host and never
+ *    throws; all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and completes asynchronously.
+ *  - The return value reports argument validation and launch errors only.
+ *    Validation runs on the host before anything is enqueued, so an error
+ *    return means nothing was launched.
+ *  - T == 0 is a valid no-op that returns OPROJ_OK (pointers are not checked).
+ *  - Device pointers must be 16-byte aligned; strides are in elements.
+ *  - Fixed in this library: head_dim 512 = nope_dim 448 + rope_dim 64,
+ *    quantisation blocks of 128 ([FUSED] asserts head_dim % block == 0 and
+ *    nope_dim % block == block - rope_dim; 448 % 128 == 64 satisfies it).
+ *    Other values return OPROJ_E_MODE.
+ *  - The FP8 format is OCP e4m3fn (max 448, no infinities).
+ *  - Inputs must be finite.  A position outside [0, max_pos) does not fault:
+ *    the affected token's scales are written as NaN (its codes are then
+ *    meaningless) so the error is visible downstream.
+ */
+#ifndef OPROJ_H
+#define OPROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum oproj_status {
+    OPROJ_OK = 0,
+    OPROJ_E_NULL = 1,  /* a required pointer is NULL */
+    OPROJ_E_SHAPE = 2, /* sizes inconsistent or outside the supported range */
+    OPROJ_E_ALIGN = 3, /* a pointer or stride breaks the 16-byte rule */
+    OPROJ_E_MODE = 4,  /* unsupported scale mode / head geometry */
+    OPROJ_E_HIP = 5    /* a HIP launch or device query failed */
+} oproj_status;
+
+/* Scale recipe ([OPROJ] compute_fp8_einsum_recipe names two):
+ *  OPROJ_SCALE_FP32: activation scale = amax / 448 as fp32 (1x128 blocks).
+ *  OPROJ_SCALE_POW2: that value rounded up to a power of two (E8M0-style),
+ *                    still stored as fp32. */
+typedef enum oproj_scale_mode { OPROJ_SCALE_FP32 = 0, OPROJ_SCALE_POW2 = 1 } oproj_scale_mode;
+
+/* Weight scale blocks:
+ *  OPROJ_WBLOCK_128x128: scale (i, kb) covers rows 128i..128i+127 of the flat
+ *                        [G*R, D] weight and columns 128kb..128kb+127;
+ *                        scales are fp32 [ceil(G*R/128), D/128] row-major.
+ *  OPROJ_WBLOCK_1x128:   scale (r, kb) per row r; fp32 [G*R, D/128] row-major.
+ * The stored scale multiplies the decoded code ([SGL] _dequant_fp8). */
+typedef enum oproj_wblock { OPROJ_WBLOCK_128x128 = 0, OPROJ_WBLOCK_1x128 = 1 } oproj_wblock;
+
+/* Shape of one call ([FUSED] parameter table; [OPROJ] deep_gemm_fp8_o_proj). */
+typedef struct oproj_shape {
+    int64_t T;               /* tokens (>= 0) */
+    int64_t n_groups;        /* G: live wo_a groups (>= 1) */
+    int64_t heads_per_group; /* hpg: 1, 2, 4 or a multiple of 8; H = G * hpg */
+    int64_t nope_dim;        /* 448 */
+    int64_t rope_dim;        /* 64 */
+    int64_t quant_block;     /* 128 */
+    int64_t o_lora_rank;     /* R: wo_a rows per group; multiple of 64 */
+    int64_t max_pos;         /* rows of the cos||sin table (> 0) */
+} oproj_shape;
+/* Derived: head_dim = nope_dim + rope_dim (512), D = hpg * head_dim,
+ * KB = D / quant_block. */
+
+/* Layout of an FP8 activation operand (codes + scales), element strides.
+ *  code  (t, g, k)  at codes [t*stride_t   + g*stride_g   + k]
+ *  scale (t, g, kb) at scales[t*s_stride_t + g*s_stride_g + kb*s_stride_kb]
+ * Passing NULL for a layout selects the default group-major layout
+ *  codes  [G][T][D]   (stride_t = D, stride_g = T*D) -- the physical layout
+ *                     [FUSED] returns ([T,G,D] viewed with strides (D, T*D, 1))
+ *  scales [G][KB][T]  (s_stride_t = 1, s_stride_kb = T, s_stride_g = KB*T),
+ *                     i.e. MN-major, tokens contiguous.
+ * stride_t and stride_g must be multiples of 16. */
+typedef struct oproj_act_layout {
+    int64_t stride_t, stride_g;
+    int64_t s_stride_t, s_stride_g, s_stride_kb;
+} oproj_act_layout;
+
+/* Steps a1 + a2 ([FUSED] fused_inv_rope_fp8_quant; [SGL] MQALayer.forward):
+ * for every token t and head h, rotate the pairs (o[t,h,448+2i], o[t,h,449+2i])
+ * by -theta(positions[t]) using c = cos_sin[p][i], s = cos_sin[p][32+i]:
+ *     e' = fma(d, s, e*c),  d' = fma(-e, s, d*c)      (fp32)
+ * keep dims 0..447, view head h as group h / hpg at offset (h % hpg)*512, and
+ * quantise each 128-wide block of each (t, g) row from the fp32 values:
+ *     amax = max(max|v|, 1e-10); s = amax / 448 (IEEE fp32; pow2: rounded up
+ *     to a power of two); code = e4m3fn(v / s), nearest even.
+ *  o          bf16 [T][H][512], contiguous
+ *  positions  int64 [T]
+ *  cos_sin    fp32 [max_pos][64]: cos[0..31] then sin[0..31]
+ *  a_codes    FP8 codes, layout `out_layout` (NULL: default group-major)
+ *  a_scales   fp32 scales, layout `out_layout`
+ * Codes and scales of groups the layout does not name are untouched. */
+oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                                  const int64_t* positions, const float* cos_sin, void* a_codes,
+                                  float* a_scales, const oproj_act_layout* out_layout,
+                                  void* stream);
+
+/* Step a3 ([OPROJ] deep_gemm_fp8_o_proj's einsum "bhr,hdr->bhd"; [GWA]):
+ *   z[t][g][n] = sum_k (decode(a[t,g,k]) * sa[t,g,k/128])
+ *                      * (decode(w[g*R+n][k]) * sw(g*R+n, k/128))
+ * with fp32 accumulation and one bf16 rounding (nearest even) at the end.
+ *  a_codes/a_scales  activation operand in layout `a_layout` (NULL: default).
+ *                    Only groups 0..G-1 are read, so a pre-quantised input
+ *                    [T][Gp][D] with Gp > G padding groups is passed with
+ *                    stride_t = Gp*D, stride_g = D ([OPROJ]: live groups first,
+ *                    padding sliced off).
+ *  w_codes   FP8 [G*R][D] row-major (K contiguous)
+ *  w_scales  fp32, blocks per `w_block`
+ *  scale_mode  OPROJ_SCALE_POW2 declares that BOTH activation and weight
+ *              scales are powers of two (they are then applied by the matrix
+ *              cores' block scaling); OPROJ_SCALE_FP32 accepts any positive
+ *              fp32 scales.
+ *  z         bf16 [T][G][R] contiguous */
+oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
+                                const float* a_scales, const oproj_act_layout* a_layout,
+                                const void* w_codes, const float* w_scales, int32_t w_block,
+                                void* z, void* stream);
+
+/* Step a4 ([SGL] MQALayer.forward applies wo_b to z.flatten(1)):
+ *   y[m][j] = sum_c x[m][c] * w[j][c], bf16 inputs, fp32 accumulation, bf16 out.
+ *  x  bf16 [M][K] row-major;  w  bf16 [N][K] row-major;  y  bf16 [M][N].
+ *  K must be a multiple of 64 and N a multiple of 16. */
+oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                                   void* y, void* stream);
+
+/* Bytes of caller-provided workspace oproj_fused needs: the FP8 codes, the
+ * scales and, when hidden > 0, the bf16 z; each region 256-byte aligned. */
+size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden);
+
+/* The whole path in one call: a1 + a2 into the workspace, a3, and when
+ * wo_b != NULL, a4 over z.flatten(1) ([OPROJ] deep_gemm_fp8_o_proj).
+ *  out  z bf16 [T][G][R] when wo_b == NULL, else y bf16 [T][hidden]
+ *  wo_b bf16 [hidden][G*R] row-major or NULL (hidden ignored when NULL)
+ * The activation scales follow scale_mode; the weight scales must match it. */
+oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                         const int64_t* positions, const float* cos_sin, const void* w_codes,
+                         const float* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
+                         void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* Offline weight preparation ([OPROJ] compute_fp8_einsum_recipe; [SGL]
+ * _setup_fp8_wo_a_scales): quantise fp32 w[rows][K] to FP8 codes with one
+ * scale per block (128x128 or 1x128 per `w_block`), scale = amax/448
+ * (pow2: rounded up to a power of two), code = e4m3fn(w / scale).
+ *  w        fp32 [rows][K];  codes FP8 [rows][K];  scales fp32 (see oproj_wblock)
+ *  K must be a multiple of 128. */
+oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
+                                   const float* w, void* codes, float* scales, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* oproj_status_string(oproj_status status);
+
+/* Library version, "MAJOR.MINOR.PATCH" (static storage). */
+const char* oproj_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPROJ_H */

@@ -69,10 +69,13 @@ def _load():
 
 
 def default_threads() -> int:
+    """Host threads the oracle uses: the affinity set, capped at 16 (the CPU
+    share of one GPU on the measurement hosts)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _p(a: np.ndarray):

@@ -1,0 +1,150 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/oproj.h
+declares, and its argument validation returns the documented status codes
+before anything touches a GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_output_projection_amd as ap
+from attention_output_projection_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oproj.h")
+
+E_OK, E_NULL, E_SHAPE, E_ALIGN, E_MODE = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ap.library_path()):
+        pytest.fail("liboproj.so is not built (run __graft_entry__.build())")
+    return ap.load_library()
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(oproj_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = _declared_symbols()
+    for s in ("oproj_inv_rope_quant", "oproj_grouped_wo_a", "oproj_fused",
+              "oproj_fused_workspace_bytes", "oproj_dense_bf16_gemm", "oproj_quantize_weight",
+              "oproj_status_string", "oproj_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in _declared_symbols():
+        assert hasattr(lib, s), s
+
+
+def test_status_strings_and_version(lib):
+    assert ap.oproj_status_string(0) == "ok"
+    assert "shape" in ap.oproj_status_string(2)
+    assert re.fullmatch(r"\d+\.\d+\.\d+", ap.oproj_version())
+
+
+def _shape(**kw):
+    base = dict(T=4, n_groups=2, heads_per_group=2, o_lora_rank=64, max_pos=4096)
+    base.update(kw)
+    return _native.Shape(**base)
+
+
+def _raw(fn, *args):
+    return getattr(ap.load_library(), fn)(*args)
+
+
+def _irq(shape, mode=0, ptrs=(0x1000,) * 5, layout=None):
+    return _raw("oproj_inv_rope_quant", ctypes.byref(shape._c()), mode, *ptrs,
+                ctypes.byref(layout._c()) if layout else None, None)
+
+
+def _gemm(shape, mode=0, wblock=0, ptrs=(0x1000,) * 5, layout=None):
+    a, sa, w, sw, z = ptrs
+    return _raw("oproj_grouped_wo_a", ctypes.byref(shape._c()), mode, a, sa,
+                ctypes.byref(layout._c()) if layout else None, w, sw, wblock, z, None)
+
+
+BAD = 0x1001  # misaligned fake address: validation rejects it before any use
+
+
+def test_inv_rope_quant_validation(lib):
+    assert _irq(_shape(T=0), ptrs=(None,) * 5) == E_OK
+    assert _irq(_shape(T=-1)) == E_SHAPE
+    assert _irq(_shape(n_groups=0)) == E_SHAPE
+    assert _irq(_shape(nope_dim=447)) == E_SHAPE  # head_dim % block != 0
+    assert _irq(_shape(nope_dim=320, rope_dim=192)) == E_SHAPE  # nope % blk != blk - rope
+    assert _irq(_shape(nope_dim=449, rope_dim=63)) == E_SHAPE  # odd rope_dim
+    assert _irq(_shape(nope_dim=960, rope_dim=64)) == E_MODE  # consistent but not 448+64
+    assert _irq(_shape(quant_block=64, nope_dim=448, rope_dim=64)) in (E_SHAPE, E_MODE)
+    assert _irq(_shape(heads_per_group=3)) == E_MODE
+    assert _irq(_shape(), mode=7) == E_MODE
+    assert _irq(_shape(), ptrs=(None, 0x1000, 0x1000, 0x1000, 0x1000)) == E_NULL
+    assert _irq(_shape(), ptrs=(BAD, 0x1000, 0x1000, 0x1000, 0x1000)) == E_ALIGN
+    assert _irq(_shape(), ptrs=(0x1000, 0x1004, 0x1000, 0x1000, 0x1000)) == E_ALIGN  # int64 positions
+    lay = _native.ActLayout(1000, 16, 1, 1, 1)  # stride_t not a multiple of 16
+    assert _irq(_shape(), layout=lay) == E_ALIGN
+    assert _irq(_shape(), layout=_native.ActLayout(-16, 16, 1, 1, 1)) == E_SHAPE
+
+
+def test_grouped_gemm_validation(lib):
+    assert _gemm(_shape(T=0), ptrs=(None,) * 5) == E_OK
+    assert _gemm(_shape(o_lora_rank=0)) == E_SHAPE
+    assert _gemm(_shape(o_lora_rank=96)) == E_SHAPE  # not a multiple of 64
+    assert _gemm(_shape(), wblock=5) == E_MODE
+    assert _gemm(_shape(), mode=3) == E_MODE
+    assert _gemm(_shape(), ptrs=(0x1000, 0x1000, None, 0x1000, 0x1000)) == E_NULL
+    assert _gemm(_shape(), ptrs=(0x1000, 0x1000, 0x1000, 0x1000, BAD)) == E_ALIGN
+    assert _gemm(_shape(), ptrs=(0x1000, 0x1002, 0x1000, 0x1000, 0x1000)) == E_ALIGN
+
+
+def test_dense_gemm_validation(lib):
+    f = lambda M, N, K, x=0x1000, w=0x1000, y=0x1000: _raw("oproj_dense_bf16_gemm", M, N, K, x, w, y, None)
+    assert f(0, 7168, 16384) == E_OK
+    assert f(-1, 7168, 16384) == E_SHAPE
+    assert f(4, 7168, 100) == E_SHAPE
+    assert f(4, 7000, 128) == E_SHAPE  # N % 16 != 0
+    assert f(4, 16, 64, x=None) == E_NULL
+    assert f(4, 16, 64, y=BAD) == E_ALIGN
+
+
+def test_fused_workspace_and_validation(lib):
+    shp = _shape(T=64, n_groups=16, heads_per_group=8, o_lora_rank=1024, max_pos=32768)
+    n0 = ap.oproj_fused_workspace_bytes(shp, 0)
+    D, KB = 4096, 32
+    assert n0 == 64 * 16 * D + 64 * 16 * KB * 4
+    n1 = ap.oproj_fused_workspace_bytes(shp, 7168)
+    assert n1 == n0 + 64 * 16 * 1024 * 2
+    assert ap.oproj_fused_workspace_bytes(_shape(o_lora_rank=10), 0) == 0
+    P = 0x1000
+
+    def fused(shape, ws_bytes, wo_b=None, hidden=0, mode=0, wblock=0, ws=P):
+        return _raw("oproj_fused", ctypes.byref(shape._c()), mode, P, P, P, P, P, wblock, wo_b, hidden,
+                    ws, ws_bytes, P, None)
+
+    assert fused(shp, n0 - 1) == E_SHAPE
+    assert fused(shp, n0, wo_b=P, hidden=7168) == E_SHAPE  # workspace lacks z
+    assert fused(shp, n1, wo_b=P, hidden=7000) == E_SHAPE
+    assert fused(shp, n0, ws=BAD) == E_ALIGN
+    assert fused(shp, n0, mode=9) == E_MODE
+    assert fused(_shape(T=0), 0) == E_OK
+
+
+def test_quantize_weight_validation(lib):
+    f = lambda rows, K, blk=0, mode=0, w=0x1000, c=0x1000, s=0x1000: _raw(
+        "oproj_quantize_weight", rows, K, blk, mode, w, c, s, None)
+    assert f(0, 128) == E_OK
+    assert f(4, 100) == E_SHAPE
+    assert f(4, 128, blk=2) == E_MODE
+    assert f(4, 128, mode=2) == E_MODE
+    assert f(4, 128, w=None) == E_NULL
+    assert f(4, 128, s=0x1002) == E_ALIGN
+
+
+def test_binding_raises_on_error_status(lib):
+    with pytest.raises(ap.OprojError) as ei:
+        ap.oproj_inv_rope_quant(_shape(heads_per_group=3), 0, 1, 1, 1, 1, 1, stream=0)
+    assert ei.value.status == E_MODE

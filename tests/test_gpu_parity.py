@@ -1,0 +1,372 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: FP32 scales bit-exact; FP8 codes identical except <= 1e-4 of elements,
+each at most one code step off; GEMM outputs E = max|y-r|/max|r| <= 1e-2
+against the oracle's fp64 result.  Full-size workloads compare every code and
+scale of the quantisation and a sample of GEMM outputs the oracle computes
+one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_output_projection_amd as ap
+import oracle
+import workloads as wl
+from tests import _util as U
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ap.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _shape(w: wl.Workload, T: int | None = None) -> ap.Shape:
+    return ap.Shape(T=w.T if T is None else T, n_groups=w.n_groups, heads_per_group=w.heads_per_group,
+                    o_lora_rank=w.o_lora_rank, max_pos=w.max_pos)
+
+
+def gpu_quant(w: wl.Workload, o: np.ndarray, pos: np.ndarray, tab: np.ndarray, pow2: bool):
+    """GPU a1+a2 in the default layout -> token-major numpy codes/scales."""
+    shp = _shape(w, o.shape[0])
+    T = o.shape[0]
+    d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
+    codes = torch.empty((w.n_groups, T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.n_groups, w.KB, T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, int(pow2), d_o, d_pos, d_tab, codes, scales)
+    return U.group_major_to_token_major(_host(codes), _host(scales))
+
+
+def gpu_weight(wmat: np.ndarray, brows: int, pow2: bool):
+    rows, K = wmat.shape
+    d_w = _dev(wmat)
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=DEV)
+    scales = torch.empty(((rows + brows - 1) // brows, K // 128), dtype=torch.float32, device=DEV)
+    blk = ap.OPROJ_WBLOCK_1x128 if brows == 1 else ap.OPROJ_WBLOCK_128x128
+    ap.oproj_quantize_weight(rows, K, blk, int(pow2), d_w, codes, scales)
+    return codes, scales
+
+
+def gpu_gemm(w: wl.Workload, qa_tm: np.ndarray, sa_tm: np.ndarray, d_wq, d_ws, brows: int,
+             pow2: bool) -> np.ndarray:
+    """GPU a3 on token-major operands [T][Gp][D] (Gp >= G) passed with explicit strides."""
+    T, Gp, D = qa_tm.shape
+    KB = D // 128
+    lay = ap.ActLayout(Gp * D, D, Gp * KB, KB, 1)
+    z = torch.empty((T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    blk = ap.OPROJ_WBLOCK_1x128 if brows == 1 else ap.OPROJ_WBLOCK_128x128
+    ap.oproj_grouped_wo_a(_shape(w, T), int(pow2), _dev(qa_tm), _dev(sa_tm), lay, d_wq, d_ws, blk, z)
+    return U.bf16_bits_to_f64(_host(z).view(np.uint16))
+
+
+# ---------------------------------------------------------------- FP8 conversion sweep
+def test_fp8_conversion_sweep_matches_oracle_encoder():
+    """Rows whose block amax is exactly 448 get scale 1, so the weight
+    quantiser's codes are the hardware conversion of the values themselves:
+    sweep fp32 values over the whole e4m3fn range (normals, subnormals, every
+    midpoint, the saturation edge)."""
+    vals, _ = np.unique(oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)), return_index=True)
+    vals = vals.astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(0)
+    x = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        rng.uniform(0, 448, 60000), np.exp(rng.uniform(-14, 6, 60000))]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) <= 448.0]
+    per_row = 127
+    n_rows = (x.size + per_row - 1) // per_row
+    buf = np.zeros(n_rows * per_row, np.float32)
+    buf[: x.size] = x
+    rows = np.concatenate([np.full((n_rows, 1), 448.0, np.float32), buf.reshape(n_rows, per_row)], axis=1)
+    codes, scales = gpu_weight(rows, 1, False)
+    s = _host(scales)
+    assert np.all(s == 1.0)
+    got = _host(codes)[:, 1:].ravel()[: x.size]
+    want = oracle.e4m3_encode(x)
+    n_bad, n, adj = U.compare_codes(got, want)
+    assert n_bad == 0, f"{n_bad}/{n} conversions differ from round-to-nearest-even"
+
+
+# ---------------------------------------------------------------- weight quantisation
+@pytest.mark.parametrize("brows,pow2", [(128, False), (1, True), (1, False), (128, True)])
+def test_weight_quant_parity(brows, pow2):
+    wmat = wl.normal_f32_bulk(wl.seed_of(90, brows + 2 * pow2), 640 * 1024, 0.02).reshape(640, 1024)
+    wmat[3, 5] = 0.9  # an outlier block
+    wmat[256:384, 128:256] = 0.0  # all-zero 128x128 block
+    codes, scales = gpu_weight(wmat, brows, pow2)
+    qr, sr = oracle.quant_weight(wmat, brows, pow2)
+    U.assert_scales_bitexact(_host(scales), sr)
+    U.assert_codes_parity(_host(codes), qr, frac=0.0)
+
+
+# ---------------------------------------------------------------- a1 + a2
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "full"])
+def test_inv_rope_quant_parity_workloads(name):
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qg, sg = gpu_quant(w, o, pos, tab, pow2=w.pow2)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=w.pow2)
+    U.assert_scales_bitexact(sg, sr)
+    U.assert_codes_parity(qg, qr)
+
+
+@pytest.mark.parametrize("T,G,hpg,pow2", [(1, 1, 1, False), (3, 2, 2, True), (5, 3, 4, False),
+                                          (77, 2, 8, False), (130, 1, 16, True), (257, 4, 8, True)])
+def test_inv_rope_quant_ragged_shapes(T, G, hpg, pow2):
+    w = wl.Workload(50 + T, f"r{T}", T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=64,
+                    max_pos=4096, positions="uniform", pow2=pow2)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    pos[0] = 0
+    pos[-1] = w.max_pos - 1
+    qg, sg = gpu_quant(w, o, pos, tab, pow2)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, hpg, pow2=pow2)
+    U.assert_scales_bitexact(sg, sr)
+    U.assert_codes_parity(qg, qr)
+
+
+def test_inv_rope_quant_degenerate_blocks():
+    """All-zero blocks, tiny and huge magnitudes, exact ties."""
+    w = wl.Workload(60, "deg", T=6, n_groups=2, heads_per_group=2, o_lora_rank=64, max_pos=64,
+                    positions="uniform")
+    o = wl.attn_out(w).copy()
+    x = wl.bf16_bits_to_f32(o).copy()
+    x[0] = 0.0  # whole token zero
+    x[1, 0, :128] = 0.0  # one zero block
+    x[2] *= 1e-30  # tiny values
+    x[3] *= 1e30  # huge values
+    x[4, :, ::2] = 0.5  # repeated values
+    o = wl.f32_to_bf16_bits(x).reshape(o.shape)
+    pos = np.array([0, 1, 2, 63, 5, 0], np.int64)
+    tab = wl.cos_sin_table(64, 64)
+    for pow2 in (False, True):
+        qg, sg = gpu_quant(w, o, pos, tab, pow2)
+        qr, sr = oracle.inv_rope_quant(o, pos, tab, 2, 2, pow2=pow2)
+        U.assert_scales_bitexact(sg, sr)
+        U.assert_codes_parity(qg, qr, frac=0.0)
+
+
+def test_inv_rope_quant_bad_position_poisons_scales():
+    w = wl.WORKLOADS["tiny"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w).copy(), wl.table(w)
+    pos[1] = w.max_pos  # out of range
+    pos[2] = -1
+    qg, sg = gpu_quant(w, o, pos, tab, False)
+    assert np.all(np.isnan(sg[1])) and np.all(np.isnan(sg[2]))
+    ok = [0, 3]
+    qr, sr = oracle.inv_rope_quant(o[ok], pos[ok], tab, w.n_groups, w.heads_per_group)
+    U.assert_scales_bitexact(sg[ok], sr)
+    U.assert_codes_parity(qg[ok], qr, frac=0.0)
+
+
+def test_inv_rope_quant_t0_is_noop():
+    w = wl.WORKLOADS["tiny"]
+    ap.oproj_inv_rope_quant(_shape(w, 0), 0, None, None, None, None, None)
+
+
+def test_inv_rope_quant_padded_layout_leaves_padding():
+    """Writing into a [T, 10, D] buffer (8 live groups) touches only groups 0..7."""
+    w = wl.WORKLOADS["pow2"].scaled(96)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    Gp = w.n_groups + w.pad_groups
+    codes = torch.full((w.T, Gp, w.D), 0x7F, dtype=torch.uint8, device=DEV)
+    scales = torch.full((w.T, Gp, w.KB), float("nan"), dtype=torch.float32, device=DEV)
+    lay = ap.ActLayout(Gp * w.D, w.D, Gp * w.KB, w.KB, 1)
+    ap.oproj_inv_rope_quant(_shape(w), 1, _dev(o.view(np.int16)), _dev(pos), _dev(tab), codes, scales, lay)
+    qg, sg = _host(codes), _host(scales)
+    assert np.all(qg[:, w.n_groups:] == 0x7F) and np.all(np.isnan(sg[:, w.n_groups:]))
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=True)
+    U.assert_scales_bitexact(sg[:, : w.n_groups], sr)
+    U.assert_codes_parity(qg[:, : w.n_groups], qr)
+
+
+# ---------------------------------------------------------------- a3
+def _weights_both(w: wl.Workload, wmat=None):
+    wmat = wl.wo_a_f32(w) if wmat is None else wmat
+    d_wq, d_ws = gpu_weight(wmat, w.w_block_rows, w.pow2)
+    qr, sr = oracle.quant_weight(wmat, w.w_block_rows, w.pow2)
+    return d_wq, d_ws, qr, sr
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_grouped_gemm_dense_parity(name):
+    """Isolated (oracle codes into the GPU GEMM) and end-to-end, every output."""
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    U.assert_scales_bitexact(_host(d_ws), swr)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
+    ref = oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank, w.w_block_rows)
+    # isolated: identical operands
+    zi = gpu_gemm(w, qr, sr, _dev(qwr), _dev(swr), w.w_block_rows, w.pow2)
+    assert U.rel_max_err(zi, ref) <= TOL
+    # end to end: GPU quantisation, GPU weights, default layout
+    shp = _shape(w)
+    codes = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), codes, scales)
+    z = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    ap.oproj_grouped_wo_a(shp, 0, codes, scales, None, d_wq, d_ws, ap.OPROJ_WBLOCK_128x128, z)
+    ze = U.bf16_bits_to_f64(_host(z).view(np.uint16))
+    e = U.rel_max_err(ze, ref)
+    assert e <= TOL, e
+
+
+@pytest.mark.parametrize("name,n_samples", [("prefill", 3000), ("full", 3000)])
+def test_grouped_gemm_sampled_parity_full_size(name, n_samples):
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
+    shp = _shape(w)
+    codes = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), codes, scales)
+    z = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    ap.oproj_grouped_wo_a(shp, 0, codes, scales, None, d_wq, d_ws, ap.OPROJ_WBLOCK_128x128, z)
+    zg = U.bf16_bits_to_f64(_host(z).view(np.uint16))
+    idx = U.sample_triples(np.random.default_rng(7), w.T, w.n_groups, w.o_lora_rank, n_samples)
+    ref = oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank, w.w_block_rows, idx=idx)
+    e = U.rel_max_err(zg[idx[:, 0], idx[:, 1], idx[:, 2]], ref)
+    assert e <= TOL, e
+    assert np.all(np.isfinite(zg))
+
+
+def test_grouped_gemm_pow2_padded_input():
+    """Pre-quantised [T, 10, D] input with NaN-poisoned padding groups, pow2
+    scales and 1x128 weight blocks (block-scaled matrix-core path)."""
+    w = wl.WORKLOADS["pow2"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    Gp = w.n_groups + w.pad_groups
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=True)
+    qpad = np.full((w.T, Gp, w.D), 0x7F, np.uint8)
+    spad = np.full((w.T, Gp, w.KB), np.nan, np.float32)
+    qpad[:, : w.n_groups], spad[:, : w.n_groups] = qr, sr
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    U.assert_scales_bitexact(_host(d_ws), swr)
+    idx = U.sample_triples(np.random.default_rng(8), w.T, w.n_groups, w.o_lora_rank, 3000)
+    ref = oracle.grouped_gemm(qpad, spad, qwr, swr, w.n_groups, w.o_lora_rank, 1, idx=idx)
+    zg = gpu_gemm(w, qpad, spad, d_wq, d_ws, 1, True)
+    assert np.all(np.isfinite(zg))
+    e = U.rel_max_err(zg[idx[:, 0], idx[:, 1], idx[:, 2]], ref)
+    assert e <= TOL, e
+
+
+@pytest.mark.parametrize("T,G,R,brows,pow2", [(1, 2, 64, 128, False), (3, 1, 128, 1, False),
+                                              (65, 2, 192, 128, False), (100, 3, 128, 1, True),
+                                              (129, 2, 128, 128, True), (300, 2, 320, 128, False),
+                                              (513, 1, 256, 1, False)])
+def test_grouped_gemm_ragged(T, G, R, brows, pow2):
+    """Ragged token counts around both kernels' tile edges, R not a multiple
+    of 128, both weight-scale layouts, both scale recipes (dense check)."""
+    w = wl.Workload(70 + T, "rag", T=T, n_groups=G, heads_per_group=8, o_lora_rank=R, max_pos=4096,
+                    positions="uniform", pow2=pow2, w_block_rows=brows)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, 8, pow2=pow2)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    ref = oracle.grouped_gemm(qr, sr, qwr, swr, G, R, brows)
+    zg = gpu_gemm(w, qr, sr, d_wq, d_ws, brows, pow2)
+    e = U.rel_max_err(zg, ref)
+    assert e <= TOL, e
+
+
+def test_grouped_gemm_group_isolation_on_gpu():
+    """Changing weight rows of other groups leaves a group's output unchanged."""
+    w = wl.Workload(80, "iso", T=40, n_groups=3, heads_per_group=8, o_lora_rank=128, max_pos=4096,
+                    positions="uniform")
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, 3, 8)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    z1 = gpu_gemm(w, qr, sr, _dev(qwr), _dev(swr), 128, False)
+    qw2 = qwr.copy()
+    qw2[: w.o_lora_rank] ^= 0x01
+    qw2[2 * w.o_lora_rank:] ^= 0x01
+    z2 = gpu_gemm(w, qr, sr, _dev(qw2), _dev(swr), 128, False)
+    assert np.array_equal(z1[:, 1], z2[:, 1])
+    assert not np.array_equal(z1[:, 0], z2[:, 0])
+
+
+# ---------------------------------------------------------------- a4 and the fused entry point
+def test_dense_bf16_gemm_parity():
+    rng = np.random.default_rng(9)
+    M, N, K = 200, 7168, 2048
+    x = wl.bf16_matrix(wl.seed_of(91, 1), M, K, 1.0)
+    wb = wl.bf16_matrix(wl.seed_of(91, 2), N, K, 0.02)
+    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ap.oproj_dense_bf16_gemm(M, N, K, _dev(x.view(np.int16)), _dev(wb.view(np.int16)), y)
+    yg = U.bf16_bits_to_f64(_host(y).view(np.uint16))
+    idx = np.stack([rng.integers(0, M, 4000), rng.integers(0, N, 4000)], axis=1)
+    idx[:2] = [[0, 0], [M - 1, N - 1]]
+    ref = oracle.dense_gemm_bf16(x, wb, idx=idx)
+    e = U.rel_max_err(yg[idx[:, 0], idx[:, 1]], ref)
+    assert e <= TOL, e
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_fused_equals_steps(name):
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    shp = _shape(w)
+    d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    zf = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    ap.oproj_fused(shp, 0, d_o, d_pos, d_tab, d_wq, d_ws, 0, None, 0, ws, nbytes, zf)
+    codes = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, 0, d_o, d_pos, d_tab, codes, scales)
+    zs = torch.empty_like(zf)
+    ap.oproj_grouped_wo_a(shp, 0, codes, scales, None, d_wq, d_ws, 0, zs)
+    assert torch.equal(zf, zs)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
+    ref = oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank)
+    assert U.rel_max_err(U.bf16_bits_to_f64(_host(zf).view(np.uint16)), ref) <= TOL
+
+
+def test_full_path_with_wo_b_sampled():
+    """The whole path at its full size: a1..a4 through oproj_fused; sampled y
+    against the oracle chain (oracle z rounded to bf16, then fp64 wo_b)."""
+    w = wl.WORKLOADS["full"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    wob = wl.wo_b_bf16(w)
+    shp = _shape(w)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, w.hidden)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    y = torch.empty((w.T, w.hidden), dtype=torch.int16, device=DEV)
+    ap.oproj_fused(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), d_wq, d_ws, 0,
+                   _dev(wob.view(np.int16)), w.hidden, ws, nbytes, y)
+    yg = U.bf16_bits_to_f64(_host(y).view(np.uint16))
+    assert np.all(np.isfinite(yg))
+    rng = np.random.default_rng(10)
+    toks = np.concatenate([[0, w.T - 1], rng.choice(w.T, 14, replace=False)])
+    qr, sr = oracle.inv_rope_quant(o[toks], pos[toks], tab, w.n_groups, w.heads_per_group)
+    zr = oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank)
+    zb = oracle.f64_to_bf16(zr).reshape(len(toks), w.n_groups * w.o_lora_rank)
+    cols = rng.integers(0, w.hidden, 128)
+    idx = np.array([[i, c] for i in range(len(toks)) for c in cols], np.int64)
+    ref = oracle.dense_gemm_bf16(zb, wob, idx=idx)
+    got = yg[toks[idx[:, 0]], idx[:, 1]]
+    e = U.rel_max_err(got, ref)
+    assert e <= TOL, e
