@@ -28,11 +28,12 @@
 //    2x2 waves of 64x64, A/B K-blocks staged through double-buffered LDS
 //    (rows padded to 144 bytes so the 16-lane fragment reads hit distinct
 //    banks), one barrier per K-block;
-//  * decode kernel (small T): 64x64 output tile per workgroup, the four waves
-//    split the K-blocks (interleaved, so their loads of one weight row are
-//    adjacent), fragments loaded straight from global memory into registers
-//    with a one-block register prefetch, partials summed through LDS.  The
-//    weight stream is the cost at small T; no LDS staging is needed.
+//  * decode kernel (small T): 64x64 output tile per workgroup, its eight
+//    waves split the K-blocks (interleaved, so their loads of one weight row
+//    are adjacent), fragments loaded straight from global memory into
+//    registers with a one-block register prefetch, partials summed through
+//    LDS.  The weight stream is the cost at small T: eight waves per CU keep
+//    enough of it in flight; no LDS staging is needed.
 // Both remap workgroups so that tiles of one group land on one XCD (a group's
 // activations and weights then stay in that XCD's L2).
 #include "device_common.hpp"
@@ -249,163 +250,207 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile_kernel(GParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel
-constexpr int DBM = 64, DBN = 64, kMaxKB = 64;
+// Decode kernel (few tokens): the weight stream is the cost.
+// Workgroup tile: one group, 64 tokens x 64 columns, the whole K.  Each
+// K-block is one pipeline stage in LDS: the 64x128-byte activation slab, the
+// 64x128-byte weight slab and the block's scales, all copied by the DMA form
+// of the global loads (global_load_lds: no staging registers).  DNS stages
+// form a ring, DNS-1 of them in flight; one s_waitcnt + barrier per K-block.
+// Every wave issues the same five copies per stage (1 KiB x 2 activation rows
+// groups, 1 KiB x 2 weight row groups, one scale gather), so the wait count is
+// a constant.  Rows are 128 bytes with the 16-byte pieces XOR-swizzled by
+// (row >> 1) & 7, which makes the 16-row fragment reads conflict-free.
+// Waves split N (wave w owns columns 16w..16w+15): no partial-sum exchange.
+constexpr int DBM = 64, DBN = 64, DNS = 4, DKS = 2;
+constexpr int DSTAGE = 64 * 128 * 2 + 1024;  // activations + weights + scales
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// LDS byte offset of a __shared__ address, made wave-uniform (an SGPR).
+__device__ __forceinline__ uint32_t lds_offset(const uint8_t* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8*)p);
+}
+
+// DMA copies global -> LDS (global_load_lds): lane i's 16 (or 4) bytes land
+// at lds + 16*i (4*i); `lds` is made wave-uniform and goes to M0.  Written as
+// asm: the compiler cannot tell these LDS writes from the ring slots being
+// read and would otherwise wait for every copy before each LDS read; all
+// waits for the copies are explicit (wait_vmcnt).  Nothing else in the
+// kernels that use them keeps a value in M0.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 template <bool MX, bool W1>
-__global__ __launch_bounds__(256) void gemm_fp8_decode_kernel(GParams p) {
-    // scale staging during the K loop, partial-sum exchange afterwards
-    __shared__ __attribute__((aligned(16))) float smem[4 * DBM * DBN];  // 64 KiB
-    float* sSA = smem;                      // [KB][64 rows]
-    float* sSW = smem + kMaxKB * DBM;       // [KB][64 cols]
+__global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int kq = tid >> 8;            // K quarter/half handled by this wave group
+    const int wave = (tid >> 6) & 3;    // column group within the tile
     const int64_t nblocks = p.G * p.mtiles * p.ntiles;
     const int64_t tile = xcd_remap(blockIdx.x, nblocks);
     const int64_t g = tile / (p.mtiles * p.ntiles);
     const int64_t mt = (tile / p.ntiles) % p.mtiles;
     const int64_t nt = tile % p.ntiles;
     const int64_t m0 = mt * DBM, n0 = nt * DBN;
+    // this wave group's K-blocks: [kb0, kb0 + nkb)
+    const int64_t kb0 = p.KB * kq / DKS;
+    const int64_t nkb = p.KB * (kq + 1) / DKS - kb0;
+    const int64_t klast = kb0 + (nkb > 0 ? nkb : 1) - 1;
 
-    // stage all scales of the tile: 64 rows x KB and 64 columns x KB
-    for (int64_t i = tid; i < p.KB * DBM; i += 256) {
-        const int64_t kb = i / DBM, r = i % DBM;
-        int64_t m = m0 + r;
-        m = m < p.T ? m : p.T - 1;
-        sSA[i] = p.sa[m * p.sst + g * p.ssg + kb * p.sskb];
-        int64_t n = n0 + r;
+    // ---- per-lane copy sources (the K-block offset is added per stage)
+    const uint8_t* asrc[2];
+    const uint8_t* wsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * wave + 8 * j + (lane >> 3);
+        const int piece = (lane & 7) ^ swz(row);
+        int64_t m = m0 + row;
+        m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
+        asrc[j] = p.a + m * p.st + g * p.sg + piece * 16;
+        int64_t n = n0 + row;
         n = n < p.R ? n : p.R - 1;
-        sSW[i] = p.sw[wscale_index(p, g * p.R + n, kb)];
+        wsrc[j] = p.w + (g * p.R + n) * p.D + piece * 16;
     }
-    __syncthreads();
-
-    const int frow = lane & 15;
-    const int fk = (lane >> 4) * 32;
-    const uint8_t* abase[4];
-    const uint8_t* bbase[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        int64_t m = m0 + s * 16 + frow;
-        m = m < p.T ? m : p.T - 1;
-        abase[s] = p.a + m * p.st + g * p.sg + fk;
-        int64_t n = n0 + s * 16 + frow;
-        n = n < p.R ? n : p.R - 1;
-        bbase[s] = p.w + (g * p.R + n) * p.D + fk;
+    // scale gather: lanes 0-15 activation scales of tokens 16w+l, lanes 16-31
+    // weight scales of columns 16w+l-16; lanes 32-63 repeat them (junk slots)
+    const float* ssrc;
+    int64_t sstep;
+    {
+        const int l = lane & 31;
+        if (l < 16) {
+            int64_t m = m0 + 16 * wave + l;
+            m = m < p.T ? m : p.T - 1;
+            ssrc = p.sa + m * p.sst + g * p.ssg;
+            sstep = p.sskb;
+        } else {
+            int64_t n = n0 + 16 * wave + (l - 16);
+            n = n < p.R ? n : p.R - 1;
+            ssrc = p.sw + wscale_index(p, g * p.R + n, 0);
+            sstep = 1;
+        }
     }
-
-    v4f acc[4][4];
+    const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
+    auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
+        int64_t kb = kb0 + i;
+        kb = kb < klast ? kb : klast;  // tail stages re-copy the last block into a dead slot
+        const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    auto load_frag = [](const uint8_t* ptr) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(ptr);
-        const uint4 hi = *reinterpret_cast<const uint4*>(ptr + 16);
-        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        for (int j = 0; j < 2; ++j) {
+            dma16(asrc[j] + kb * 128, st + (16 * wave + 8 * j) * 128);
+            dma16(wsrc[j] + kb * 128, st + 8192 + (16 * wave + 8 * j) * 128);
+        }
+        dma4(ssrc + kb * sstep, st + 16384 + 256 * wave);
     };
 
-    v8i ca[4], cb[4], na[4], nb[4];
-    int64_t kb = wave;
-    if (kb < p.KB) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            ca[s] = load_frag(abase[s] + kb * 128);
-            cb[s] = load_frag(bbase[s] + kb * 128);
+    for (int s = 0; s < DNS - 1; ++s) issue(s, s);
+
+    v4f acc[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) acc[mi] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int p0 = 2 * (lane >> 4);
+    const int64_t nstages = p.KB / DKS + 1;  // >= nkb for every group: same barrier count
+    for (int64_t i = 0; i < nstages; ++i) {
+        wait_vmcnt<5 * (DNS - 2)>();  // this wave's copies of stage i have landed
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence: the
+                                       // prefetches stay in flight)
+        issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
+        if (i >= nkb) continue;        // uniform per wave group
+        const uint8_t* st = ring[kq][i % DNS];
+        v8i bfr;
+        {
+            const int r = 16 * wave + frow;
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * (p0 ^ swz(r)));
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
+            bfr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        const float* sc = reinterpret_cast<const float*>(st + 16384);
+        const float swv = sc[64 * wave + 16 + (W1 || MX ? frow : 0)];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = 16 * mi + frow;
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * (p0 ^ swz(r)));
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
+            const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if constexpr (MX) {
+                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], e8m0_of(sc[64 * mi + frow]), e8m0_of(swv));
+            } else {
+                const float4 t4 = *reinterpret_cast<const float4*>(&sc[64 * mi + 4 * (lane >> 4)]);
+                const float cmb[4] = {t4.x * swv, t4.y * swv, t4.z * swv, t4.w * swv};
+                const v4f pp = mfma_fp8(af, bfr, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) acc[mi][i2] = __builtin_fmaf(pp[i2], cmb[i2], acc[mi][i2]);
+            }
         }
     }
-    for (; kb < p.KB; kb += 4) {
-        const int64_t kn = kb + 4;
-        if (kn < p.KB) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                na[s] = load_frag(abase[s] + kn * 128);
-                nb[s] = load_frag(bbase[s] + kn * 128);
-            }
-        }
-        const float* sak = sSA + kb * DBM;
-        const float* swk = sSW + kb * DBN;
-        if constexpr (MX) {
-            int ea[4], eb[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                ea[s] = e8m0_of(sak[s * 16 + frow]);
-                eb[s] = e8m0_of(swk[s * 16 + frow]);
-            }
+    wait_vmcnt<0>();  // no copy may still be writing LDS
+    __syncthreads();
+
+    // ---- sum the K groups through LDS (ring 0 of group 0 is free now)
+    float* red = reinterpret_cast<float*>(&ring[0][0][0]);
+    if constexpr (DKS > 1) {
+        if (kq > 0) {
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = mfma_fp8_mx(ca[mi], cb[ni], acc[mi][ni], ea[mi], eb[ni]);
-        } else {
-            float sa4[4][4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const float4 t4 = *reinterpret_cast<const float4*>(&sak[mi * 16 + 4 * (lane >> 4)]);
-                sa4[mi][0] = t4.x;
-                sa4[mi][1] = t4.y;
-                sa4[mi][2] = t4.z;
-                sa4[mi][3] = t4.w;
-            }
-            if constexpr (W1) {
-                float swv[4];
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) swv[ni] = swk[ni * 16 + frow];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4f pp = mfma_fp8(ca[mi], cb[ni], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mi][ni][i] = __builtin_fmaf(pp[i], sa4[mi][i] * swv[ni], acc[mi][ni][i]);
-                    }
-            } else {
-                const float sws = swk[0];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    float cmb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) cmb[i] = sa4[mi][i] * sws;
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4f pp = mfma_fp8(ca[mi], cb[ni], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mi][ni][i] = __builtin_fmaf(pp[i], cmb[i], acc[mi][ni][i]);
-                    }
-                }
-            }
+                for (int i = 0; i < 4; ++i) red[((kq - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i] = acc[mi][i];
         }
-        if (kn < p.KB) {
+        __syncthreads();
+        if (kq > 0) return;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                ca[s] = na[s];
-                cb[s] = nb[s];
-            }
-        }
+        for (int q = 1; q < DKS; ++q)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mi][i] += red[((q - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i];
     }
 
-    // sum the four K-slices: every wave parks its partial tile in LDS
-    __syncthreads();  // scale staging is dead from here on
+    // ---- bf16 results of this wave's 16 columns
+    const int64_t col = n0 + 16 * wave + frow;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                smem[wave * (DBM * DBN) + (((mi * 4 + ni) * 4 + i) * 64) + lane] = acc[mi][ni][i];
-    __syncthreads();
-    const int col = tid & 63;
-#pragma unroll 4
-    for (int rr = 0; rr < 16; ++rr) {
-        const int row = (tid >> 6) + 4 * rr;
-        const int mi = row >> 4, i = row & 3, ln = 16 * ((row & 15) >> 2) + (col & 15), ni = col >> 4;
-        const int idx = ((mi * 4 + ni) * 4 + i) * 64 + ln;
-        const float s = smem[idx] + smem[DBM * DBN + idx] + smem[2 * DBM * DBN + idx] +
-                        smem[3 * DBM * DBN + idx];
-        const int64_t t = m0 + row, n = n0 + col;
-        if (t < p.T && n < p.R) p.z[(t * p.G + g) * p.R + n] = (uint16_t)f32_to_bf16_bits(s);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + mi * 16 + 4 * (lane >> 4) + i;
+            if (row < p.T && col < p.R) p.z[(row * p.G + g) * p.R + col] = (uint16_t)f32_to_bf16_bits(acc[mi][i]);
+        }
+}
+
+void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.G * p.mtiles * p.ntiles)), block(DKS * 256);
+    if (mx) {
+        if (w1)
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, false>), grid, block, 0, stream, p);
+    } else {
+        if (w1)
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, false>), grid, block, 0, stream, p);
     }
 }
 
@@ -429,22 +474,12 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.ssg = a.lay.s_stride_g;
     p.sskb = a.lay.s_stride_kb;
     p.w_shift = a.w_1x128 ? 0 : 7;
-    const bool decode = a.T <= 128 && p.KB <= kMaxKB;
+    // decode kernel for few tokens (the weight stream dominates), tile kernel otherwise
+    const bool decode = a.T <= 128;
     if (decode) {
         p.mtiles = (a.T + DBM - 1) / DBM;
         p.ntiles = (a.R + DBN - 1) / DBN;
-        const dim3 grid((unsigned)(p.G * p.mtiles * p.ntiles));
-        if (a.mx) {
-            if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, true>), grid, dim3(256), 0, stream, p);
-            else
-                hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, false>), grid, dim3(256), 0, stream, p);
-        } else {
-            if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, true>), grid, dim3(256), 0, stream, p);
-            else
-                hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, false>), grid, dim3(256), 0, stream, p);
-        }
+        launch_decode(p, a.mx != 0, a.w_1x128 != 0, stream);
     } else {
         p.mtiles = (a.T + TBM - 1) / TBM;
         p.ntiles = (a.R + TBN - 1) / TBN;
