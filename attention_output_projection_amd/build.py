@@ -16,6 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["rope_quant.hip", "gemm_fp8.hip", "gemm_bf16.hip", "api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    # matrix-core results stay in VGPRs (the block-scale promotion reads them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC,

@@ -128,6 +128,15 @@ oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, co
     if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(z) ||
         (reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scales) & 3u))
         return OPROJ_E_ALIGN;
+    {
+        // the kernels address operands as a uniform base plus 32-bit lane offsets
+        const oproj::ActLayout l = to_layout(a_layout, shape);
+        const int64_t D = shape->heads_per_group * 512, KB = D / 128, lim = int64_t(1) << 32;
+        const int64_t rows = shape->n_groups * shape->o_lora_rank;
+        if ((shape->T - 1) * l.stride_t + D >= lim || (shape->T - 1) * l.s_stride_t * 4 + 4 >= lim ||
+            rows * D >= lim || rows * KB * 4 >= lim)
+            return OPROJ_E_SHAPE;
+    }
     oproj::GroupedGemmArgs a;
     a.T = shape->T;
     a.G = shape->n_groups;

@@ -23,17 +23,15 @@
 //    v_mfma_scale_f32_16x16x128_f8f6f4 applies the E8M0 exponents of sa and
 //    sw in the matrix core and accumulates directly; no VALU work per block.
 //
-// Two kernels share this machinery:
-//  * tile kernel (large T): 128x128 output tile per 256-thread workgroup,
-//    2x2 waves of 64x64, A/B K-blocks staged through double-buffered LDS
-//    (rows padded to 144 bytes so the 16-lane fragment reads hit distinct
-//    banks), one barrier per K-block;
-//  * decode kernel (small T): 64x64 output tile per workgroup, its eight
-//    waves split the K-blocks (interleaved, so their loads of one weight row
-//    are adjacent), fragments loaded straight from global memory into
-//    registers with a one-block register prefetch, partials summed through
-//    LDS.  The weight stream is the cost at small T: eight waves per CU keep
-//    enough of it in flight; no LDS staging is needed.
+// Two kernels share this machinery, both fed by direct global->LDS copies
+// (global_load_lds) into rings of 128-byte rows whose 16-byte pieces are
+// XOR-swizzled so fragment reads hit distinct banks:
+//  * tile kernel (large T): 256x256 output tile per 512-thread workgroup,
+//    eight waves of 128x64, one K-block per stage, double-buffered;
+//  * decode kernel (small T): 64x64 output tile per workgroup, two K-groups
+//    of four waves (16 columns each) with a four-stage ring each, the two
+//    partial tiles summed through LDS at the end.  The weight stream is the
+//    cost at small T; the deep ring keeps enough of it in flight.
 // Both remap workgroups so that tiles of one group land on one XCD (a group's
 // activations and weights then stay in that XCD's L2).
 #include "device_common.hpp"
@@ -76,194 +74,7 @@ __device__ __forceinline__ int64_t wscale_index(const GParams& p, int64_t wrow, 
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel
-constexpr int TBM = 128, TBN = 128, LROW = 144;
-
-template <bool MX, bool W1>
-__global__ __launch_bounds__(256) void gemm_fp8_tile_kernel(GParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][TBM * LROW];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][TBN * LROW];
-    __shared__ __attribute__((aligned(16))) float sSA[2][TBM];
-    __shared__ __attribute__((aligned(16))) float sSW[2][TBN];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t nblocks = p.G * p.mtiles * p.ntiles;
-    const int64_t tile = xcd_remap(blockIdx.x, nblocks);
-    const int64_t g = tile / (p.mtiles * p.ntiles);
-    const int64_t mt = (tile / p.ntiles) % p.mtiles;
-    const int64_t nt = tile % p.ntiles;
-    const int64_t m0 = mt * TBM, n0 = nt * TBN;
-
-    // global -> register staging: 1024 16-byte chunks per operand, 4 per thread
-    const int crow = tid >> 3;       // + 32*i
-    const int ccol = (tid & 7) * 16; // byte offset in the 128-byte K-block row
-    const uint8_t* aptr[4];
-    const uint8_t* bptr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t m = m0 + crow + 32 * i;
-        m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
-        aptr[i] = p.a + m * p.st + g * p.sg + ccol;
-        int64_t n = n0 + crow + 32 * i;
-        n = n < p.R ? n : p.R - 1;
-        bptr[i] = p.w + (g * p.R + n) * p.D + ccol;
-    }
-    const float* saptr = nullptr;
-    const float* swptr = nullptr;
-    if (tid < TBM) {
-        int64_t m = m0 + tid;
-        m = m < p.T ? m : p.T - 1;
-        saptr = p.sa + m * p.sst + g * p.ssg;
-    } else {
-        int64_t n = n0 + (tid - TBM);
-        n = n < p.R ? n : p.R - 1;
-        swptr = p.sw + wscale_index(p, g * p.R + n, 0);
-    }
-
-    // staging registers; macros (not lambdas) keep them out of scratch
-    uint4 ra[4], rb[4];
-    float rs;
-#define OPROJ_GLOAD(kb)                                                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                \
-        ra[i] = *reinterpret_cast<const uint4*>(aptr[i] + (kb) * 128);             \
-        rb[i] = *reinterpret_cast<const uint4*>(bptr[i] + (kb) * 128);             \
-    }                                                                              \
-    rs = (tid < TBM) ? saptr[(kb) * p.sskb] : swptr[(kb)];
-#define OPROJ_SWRITE(buf)                                                          \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                \
-        *reinterpret_cast<uint4*>(&sA[buf][(crow + 32 * i) * LROW + ccol]) = ra[i]; \
-        *reinterpret_cast<uint4*>(&sB[buf][(crow + 32 * i) * LROW + ccol]) = rb[i]; \
-    }                                                                              \
-    if (tid < TBM)                                                                 \
-        sSA[buf][tid] = rs;                                                        \
-    else                                                                           \
-        sSW[buf][tid - TBM] = rs;
-
-    v4f acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int frow = lane & 15;
-    const int fk = (lane >> 4) * 32;
-
-    OPROJ_GLOAD(0);
-    OPROJ_SWRITE(0);
-    __syncthreads();
-
-    for (int64_t kb = 0; kb < p.KB; ++kb) {
-        const int buf = (int)(kb & 1);
-        // unconditional (clamped) prefetch keeps the staging registers out of scratch
-        OPROJ_GLOAD(kb + 1 < p.KB ? kb + 1 : kb);
-
-        v8i af[4], bfr[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const uint8_t* src = &sA[buf][(wm * 64 + mi * 16 + frow) * LROW + fk];
-            const uint4 lo = *reinterpret_cast<const uint4*>(src);
-            const uint4 hi = *reinterpret_cast<const uint4*>(src + 16);
-            af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const uint8_t* src = &sB[buf][(wn * 64 + ni * 16 + frow) * LROW + fk];
-            const uint4 lo = *reinterpret_cast<const uint4*>(src);
-            const uint4 hi = *reinterpret_cast<const uint4*>(src + 16);
-            bfr[ni] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-
-        if constexpr (MX) {
-            int ea[4], eb[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) ea[mi] = e8m0_of(sSA[buf][wm * 64 + mi * 16 + frow]);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) eb[ni] = e8m0_of(sSW[buf][wn * 64 + ni * 16 + frow]);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = mfma_fp8_mx(af[mi], bfr[ni], acc[mi][ni], ea[mi], eb[ni]);
-        } else {
-            float sa4[4][4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const float4 t4 = *reinterpret_cast<const float4*>(
-                    &sSA[buf][wm * 64 + mi * 16 + 4 * (lane >> 4)]);
-                sa4[mi][0] = t4.x;
-                sa4[mi][1] = t4.y;
-                sa4[mi][2] = t4.z;
-                sa4[mi][3] = t4.w;
-            }
-            if constexpr (W1) {
-                float swv[4];
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) swv[ni] = sSW[buf][wn * 64 + ni * 16 + frow];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4f pp = mfma_fp8(af[mi], bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mi][ni][i] = __builtin_fmaf(pp[i], sa4[mi][i] * swv[ni], acc[mi][ni][i]);
-                    }
-            } else {
-                const float sws = sSW[buf][wn * 64];  // one weight scale per 64-column span
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    float cmb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) cmb[i] = sa4[mi][i] * sws;
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4f pp = mfma_fp8(af[mi], bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mi][ni][i] = __builtin_fmaf(pp[i], cmb[i], acc[mi][ni][i]);
-                    }
-                }
-            }
-        }
-
-        if (kb + 1 < p.KB) { OPROJ_SWRITE(buf ^ 1); }
-        __syncthreads();
-    }
-
-#undef OPROJ_GLOAD
-#undef OPROJ_SWRITE
-    // epilogue: bf16 (nearest even), z[t][g][n]
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
-                const int64_t col = n0 + wn * 64 + ni * 16 + frow;
-                if (row < p.T && col < p.R)
-                    p.z[(row * p.G + g) * p.R + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
-            }
-}
-
-// ---------------------------------------------------------------------------
-// Decode kernel (few tokens): the weight stream is the cost.
-// Workgroup tile: one group, 64 tokens x 64 columns, the whole K.  Each
-// K-block is one pipeline stage in LDS: the 64x128-byte activation slab, the
-// 64x128-byte weight slab and the block's scales, all copied by the DMA form
-// of the global loads (global_load_lds: no staging registers).  DNS stages
-// form a ring, DNS-1 of them in flight; one s_waitcnt + barrier per K-block.
-// Every wave issues the same five copies per stage (1 KiB x 2 activation rows
-// groups, 1 KiB x 2 weight row groups, one scale gather), so the wait count is
-// a constant.  Rows are 128 bytes with the 16-byte pieces XOR-swizzled by
-// (row >> 1) & 7, which makes the 16-row fragment reads conflict-free.
-// Waves split N (wave w owns columns 16w..16w+15): no partial-sum exchange.
-constexpr int DBM = 64, DBN = 64, DNS = 4, DKS = 2;
-constexpr int DSTAGE = 64 * 128 * 2 + 1024;  // activations + weights + scales
-
+// Shared pipeline helpers
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // LDS byte offset of a __shared__ address, made wave-uniform (an SGPR).
@@ -298,7 +109,223 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// 16-byte piece swizzle of a 128-byte LDS row.  A fragment read (ds_read_b128)
+// has the lanes of 16 consecutive rows fetch the same piece; XOR with
+// (row & 7) ^ ((row >> 3) & 1) puts any 8 consecutive rows on 8 different
+// pieces and any 16 consecutive rows on 16 different (row parity, piece)
+// bank groups, so the reads are conflict-free whether the LDS serves 8 lanes
+// over 32 banks or 16 lanes over 64 banks per cycle.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// DMA copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (no per-copy vector address arithmetic).  The base is passed
+// through readfirstlane so it always lands in scalar registers.
+__device__ __forceinline__ uint64_t uniform64(const void* p) {
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform64(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform64(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel (large T): 256x256 output tile per 512-thread workgroup, eight
+// waves as 2 (M) x 4 (N) of 128x64 (32 MFMAs per K-block per wave, 128 fp32
+// accumulators in VGPRs), two waves per SIMD.  The tile and wave shapes keep
+// LDS reads per MFMA low: per K-block the workgroup reads 192 KiB of
+// fragments and copies 64 KiB for 2048 MFMA cycles per SIMD.  Each K-block is
+// one pipeline stage (256x128-byte activation slab, 256x128-byte weight slab,
+// the block's scales), DMA-copied into a double-buffered LDS ring with
+// XOR-swizzled 128-byte rows; one s_waitcnt + bare barrier per K-block.
+constexpr int TBM = 256, TBN = 256, TNS = 2, TNW = 8;
+constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
+constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
+constexpr int TCOPIES = 4 + 4 + 1;  // copy instructions per wave per stage
+
+template <bool MX, bool W1>
+__global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[TNS][TSTAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t nblocks = p.G * p.mtiles * p.ntiles;
+    const int64_t tile = xcd_remap(blockIdx.x, nblocks);
+    const int64_t g = tile / (p.mtiles * p.ntiles);
+    const int64_t mt = (tile / p.ntiles) % p.mtiles;
+    const int64_t nt = tile % p.ntiles;
+    const int64_t m0 = mt * TBM, n0 = nt * TBN;
+
+    // ---- copy plan.  Wave w copies activation rows 32w..32w+31 and weight
+    // rows 32w..32w+31 (4 x 8 rows each) and one scale gather of every stage
+    // (waves 0-3: activation scales of rows 64w..64w+63; waves 4-7: weight
+    // scales of columns 64(w-4)..+63).  Sources are uniform bases (advanced
+    // per K-block) plus fixed 32-bit lane offsets (the host keeps every
+    // offset below 2^32).
+    const uint8_t* abase = p.a + g * p.sg;
+    const uint8_t* wbase = p.w + g * p.R * p.D;
+    uint32_t aoff[4], woff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 32 * wave + 8 * j + (lane >> 3);
+        int64_t m = m0 + row;
+        m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
+        aoff[j] = (uint32_t)(m * p.st + ((lane & 7) ^ swz(row)) * 16);
+        int64_t n = n0 + row;
+        n = n < p.R ? n : p.R - 1;
+        woff[j] = (uint32_t)(n * p.D + ((lane & 7) ^ swz(row)) * 16);
+    }
+    const uint8_t* sbase;
+    uint32_t soff;
+    int64_t sstep;  // bytes per K-block
+    uint32_t sdst;
+    if (wave < 4) {
+        int64_t m = m0 + 64 * wave + lane;
+        m = m < p.T ? m : p.T - 1;
+        sbase = reinterpret_cast<const uint8_t*>(p.sa + g * p.ssg);
+        soff = (uint32_t)(m * p.sst * 4);
+        sstep = p.sskb * 4;
+        sdst = TSS + 256 * wave;
+    } else {
+        int64_t n = n0 + 64 * (wave - 4) + lane;
+        n = n < p.R ? n : p.R - 1;
+        sbase = reinterpret_cast<const uint8_t*>(p.sw);
+        soff = (uint32_t)(wscale_index(p, g * p.R + n, 0) * 4);
+        sstep = 4;
+        sdst = TSW + 256 * (wave - 4);
+    }
+    const uint32_t ring0 = lds_offset(&ring[0][0]);
+    const uint32_t adst = ring0 + TSA + 32 * wave * 128, wdst = ring0 + TSB + 32 * wave * 128;
+    auto issue = [&](int64_t kb, int slot) __attribute__((always_inline)) {
+        kb = kb < p.KB ? kb : p.KB - 1;  // tail stages re-copy the last block into a dead slot
+        const uint32_t so = (uint32_t)(slot * TSTAGE);
+        const uint8_t* ab = abase + kb * 128;
+        const uint8_t* wb = wbase + kb * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16s(ab, aoff[j], adst + so + j * 1024);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16s(wb, woff[j], wdst + so + j * 1024);
+        dma4s(sbase + kb * sstep, soff, ring0 + so + sdst);
+    };
+
+    issue(0, 0);
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // fragment addressing: rows 16k + frow share the swizzle of frow, so a
+    // lane's two piece offsets are fixed and subtiles step by 2 KiB
+    const int frow = lane & 15;
+    const int p0 = 2 * (lane >> 4);
+    const int lo_off = frow * 128 + 16 * (p0 ^ swz(frow));
+    const int hi_off = frow * 128 + 16 * ((p0 + 1) ^ swz(frow));
+    const int sa_off = 4 * (128 * wm + 4 * (lane >> 4));  // activation scales of the lane's rows
+    auto frag = [&](const uint8_t* base) __attribute__((always_inline)) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + lo_off);
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + hi_off);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    for (int64_t kb = 0; kb < p.KB; ++kb) {
+        wait_vmcnt<0>();               // this wave's copies of stage kb have landed
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
+        issue(kb + 1, (int)((kb + 1) & 1));
+        const uint8_t* st = ring[kb & 1];
+        const uint8_t* sta = st + TSA + 128 * wm * 128;
+        const uint8_t* stb = st + TSB + 64 * wn * 128;
+        const float* sca = reinterpret_cast<const float*>(st + TSS);
+        const float* scw = reinterpret_cast<const float*>(st + TSW);
+        v8i bfr[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) bfr[ni] = frag(stb + ni * 2048);
+        if constexpr (MX) {
+            int eb[4];
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) eb[ni] = e8m0_of(scw[64 * wn + 16 * ni + frow]);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const v8i af = frag(sta + mi * 2048);
+                const int ea = e8m0_of(sca[128 * wm + 16 * mi + frow]);
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
+            }
+        } else if constexpr (W1) {
+            float swv[4];
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const v8i af = frag(sta + mi * 2048);
+                const float4 t4 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(sca) + sa_off + 64 * mi);
+                const float sa4[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const v4f pp = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[mi][ni][i] = __builtin_fmaf(pp[i], sa4[i] * swv[ni], acc[mi][ni][i]);
+                }
+            }
+        } else {
+            const float sws = scw[64 * wn];  // one weight scale per 64-column span
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const v8i af = frag(sta + mi * 2048);
+                const float4 t4 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(sca) + sa_off + 64 * mi);
+                const float cmb[4] = {t4.x * sws, t4.y * sws, t4.z * sws, t4.w * sws};
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const v4f pp = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[mi][ni][i] = __builtin_fmaf(pp[i], cmb[i], acc[mi][ni][i]);
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
+
+    // epilogue: bf16 (nearest even), z[t][g][n]
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
+                const int64_t col = n0 + 64 * wn + 16 * ni + frow;
+                if (row < p.T && col < p.R)
+                    p.z[(row * p.G + g) * p.R + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
+            }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel (few tokens): the weight stream is the cost.
+// Workgroup tile: one group, 64 tokens x 64 columns, the whole K.  Each
+// K-block is one pipeline stage in LDS: the 64x128-byte activation slab, the
+// 64x128-byte weight slab and the block's scales, all copied by the DMA form
+// of the global loads (global_load_lds: no staging registers).  DNS stages
+// form a ring, DNS-1 of them in flight; one s_waitcnt + barrier per K-block.
+// Every wave issues the same five copies per stage (1 KiB x 2 activation rows
+// groups, 1 KiB x 2 weight row groups, one scale gather), so the wait count is
+// a constant.  Rows are 128 bytes with the 16-byte pieces XOR-swizzled by
+// row & 7, which makes the fragment reads conflict-free.
+// Waves split N (wave w owns columns 16w..16w+15): no partial-sum exchange.
+constexpr int DBM = 64, DBN = 64, DNS = 4, DKS = 2;
+constexpr int DSTAGE = 64 * 128 * 2 + 1024;  // activations + weights + scales
 
 template <bool MX, bool W1>
 __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
@@ -486,14 +513,14 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
         const dim3 grid((unsigned)(p.G * p.mtiles * p.ntiles));
         if (a.mx) {
             if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, true>), grid, dim3(256), 0, stream, p);
+                hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, true>), grid, dim3(TNW * 64), 0, stream, p);
             else
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, false>), grid, dim3(256), 0, stream, p);
+                hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, false>), grid, dim3(TNW * 64), 0, stream, p);
         } else {
             if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, true>), grid, dim3(256), 0, stream, p);
+                hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, true>), grid, dim3(TNW * 64), 0, stream, p);
             else
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, false>), grid, dim3(256), 0, stream, p);
+                hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, false>), grid, dim3(TNW * 64), 0, stream, p);
         }
     }
     return hipGetLastError();
