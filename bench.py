@@ -97,6 +97,21 @@ def cpu_baseline(w, o, pos, tab, wmat, max_tokens: int):
                       f"grouped wo_a in fp64, {dt:.2f} s"}
 
 
+def copy_calibration(torch, dev, mib: int) -> int:
+    """A plain copy of a known size: each launch reads and writes mib MiB.
+    Its FETCH_SIZE / WRITE_SIZE counters calibrate the HBM byte counts taken
+    on the path's kernels."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"8 copies of {n} bytes")
+    return 0
+
+
 def main() -> int:
     ap_ = argparse.ArgumentParser()
     ap_.add_argument("--gpus", type=int, default=1)
@@ -107,6 +122,8 @@ def main() -> int:
     ap_.add_argument("--kernel-reps", type=int, default=50, help="graph replays per kernel timing")
     ap_.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
     ap_.add_argument("--no-cpu-baseline", action="store_true")
+    ap_.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                     help="only run plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap_.parse_args()
 
     if args.gpus != 1:
@@ -122,8 +139,10 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    ap.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        return copy_calibration(torch, dev, args.copy_calibration)
+    ap.load_library()
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: T={w.T} G={w.n_groups} hpg={w.heads_per_group} D={w.D} R={w.o_lora_rank}")
 
@@ -289,8 +308,7 @@ def main() -> int:
     tokens_per_s = w.T / (ms_per_step * 1e-3)
     gemm_tflops = kernel_flops_gemm(w) / (ms_per_step * 1e9)
     result = {
-        "metric": "tokens/s of inverse RoPE + FP8 quant + grouped wo_a"
-                  + (" + wo_b" if wob is not None else ""),
+        "metric": "tokens/s and TFLOP/s of inv-RoPE+FP8 quant+grouped wo_a; % of HBM/FP8 roofline",
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
