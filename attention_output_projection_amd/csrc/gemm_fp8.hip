@@ -148,10 +148,15 @@ __device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t
 // one pipeline stage (256x128-byte activation slab, 256x128-byte weight slab,
 // the block's scales), DMA-copied into a double-buffered LDS ring with
 // XOR-swizzled 128-byte rows; one s_waitcnt + bare barrier per K-block.
+//
+// Waves 0-3 issue all copies of a stage (18 each, right after the barrier);
+// waves 4-7 only compute.  A copy waits at issue while the CU's memory
+// pipeline is full, which at these tile sizes lasts longer than a K-block's
+// MFMAs; a copying wave therefore starts its MFMAs late, and its SIMD partner
+// (a wave that never copies) keeps the matrix core busy meanwhile.
 constexpr int TBM = 256, TBN = 256, TNS = 2, TNW = 8;
 constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
 constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
-constexpr int TCOPIES = 4 + 4 + 1;  // copy instructions per wave per stage
 
 template <bool MX, bool W1>
 __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
@@ -167,59 +172,51 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     const int64_t nt = tile % p.ntiles;
     const int64_t m0 = mt * TBM, n0 = nt * TBN;
 
-    // ---- copy plan.  Wave w copies activation rows 32w..32w+31 and weight
-    // rows 32w..32w+31 (4 x 8 rows each) and one scale gather of every stage
-    // (waves 0-3: activation scales of rows 64w..64w+63; waves 4-7: weight
-    // scales of columns 64(w-4)..+63).  Sources are uniform bases (advanced
-    // per K-block) plus fixed 32-bit lane offsets (the host keeps every
-    // offset below 2^32).
+    // ---- copy plan.  Copying wave c (0-3) moves activation rows 64c..64c+63
+    // and weight rows 64c..64c+63 (8 rows of 128 bytes per instruction) and
+    // the scales of those rows and columns.  Sources are uniform bases
+    // (advanced per K-block) plus fixed 32-bit lane offsets (the host keeps
+    // every offset below 2^32).
+    const bool copier = wave < 4;  // wave-uniform
     const uint8_t* abase = p.a + g * p.sg;
     const uint8_t* wbase = p.w + g * p.R * p.D;
-    uint32_t aoff[4], woff[4];
+    const uint8_t* sabase = reinterpret_cast<const uint8_t*>(p.sa + g * p.ssg);
+    const uint8_t* swbase = reinterpret_cast<const uint8_t*>(p.sw);
+    uint32_t off[16], soffa = 0, soffw = 0;
+    if (copier) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 32 * wave + 8 * j + (lane >> 3);
-        int64_t m = m0 + row;
-        m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
-        aoff[j] = (uint32_t)(m * p.st + ((lane & 7) ^ swz(row)) * 16);
-        int64_t n = n0 + row;
-        n = n < p.R ? n : p.R - 1;
-        woff[j] = (uint32_t)(n * p.D + ((lane & 7) ^ swz(row)) * 16);
-    }
-    const uint8_t* sbase;
-    uint32_t soff;
-    int64_t sstep;  // bytes per K-block
-    uint32_t sdst;
-    if (wave < 4) {
+        for (int j = 0; j < 8; ++j) {
+            const int row = 64 * wave + 8 * j + (lane >> 3);
+            int64_t m = m0 + row;
+            m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
+            off[j] = (uint32_t)(m * p.st + ((lane & 7) ^ swz(row)) * 16);
+            int64_t n = n0 + row;
+            n = n < p.R ? n : p.R - 1;
+            off[8 + j] = (uint32_t)(n * p.D + ((lane & 7) ^ swz(row)) * 16);
+        }
         int64_t m = m0 + 64 * wave + lane;
         m = m < p.T ? m : p.T - 1;
-        sbase = reinterpret_cast<const uint8_t*>(p.sa + g * p.ssg);
-        soff = (uint32_t)(m * p.sst * 4);
-        sstep = p.sskb * 4;
-        sdst = TSS + 256 * wave;
-    } else {
-        int64_t n = n0 + 64 * (wave - 4) + lane;
+        soffa = (uint32_t)(m * p.sst * 4);
+        int64_t n = n0 + 64 * wave + lane;
         n = n < p.R ? n : p.R - 1;
-        sbase = reinterpret_cast<const uint8_t*>(p.sw);
-        soff = (uint32_t)(wscale_index(p, g * p.R + n, 0) * 4);
-        sstep = 4;
-        sdst = TSW + 256 * (wave - 4);
+        soffw = (uint32_t)(wscale_index(p, g * p.R + n, 0) * 4);
     }
     const uint32_t ring0 = lds_offset(&ring[0][0]);
-    const uint32_t adst = ring0 + TSA + 32 * wave * 128, wdst = ring0 + TSB + 32 * wave * 128;
+    const uint32_t adst = ring0 + TSA + 64 * (wave & 3) * 128, wdst = ring0 + TSB + 64 * (wave & 3) * 128;
     auto issue = [&](int64_t kb, int slot) __attribute__((always_inline)) {
-        kb = kb < p.KB ? kb : p.KB - 1;  // tail stages re-copy the last block into a dead slot
+        kb = kb < p.KB ? kb : p.KB - 1;  // past the end: re-copy the last block into a dead slot
         const uint32_t so = (uint32_t)(slot * TSTAGE);
         const uint8_t* ab = abase + kb * 128;
         const uint8_t* wb = wbase + kb * 128;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16s(ab, aoff[j], adst + so + j * 1024);
+        for (int j = 0; j < 8; ++j) dma16s(ab, off[j], adst + so + j * 1024);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16s(wb, woff[j], wdst + so + j * 1024);
-        dma4s(sbase + kb * sstep, soff, ring0 + so + sdst);
+        for (int j = 0; j < 8; ++j) dma16s(wb, off[8 + j], wdst + so + j * 1024);
+        dma4s(sabase + kb * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
+        dma4s(swbase + kb * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
     };
 
-    issue(0, 0);
+    if (copier) issue(0, 0);
 
     v4f acc[8][4];
 #pragma unroll
@@ -241,9 +238,9 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     };
 
     for (int64_t kb = 0; kb < p.KB; ++kb) {
-        wait_vmcnt<0>();               // this wave's copies of stage kb have landed
+        if (copier) wait_vmcnt<0>();   // this wave's copies of stage kb have landed
         __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
-        issue(kb + 1, (int)((kb + 1) & 1));
+        if (copier) issue(kb + 1, (int)((kb + 1) & 1));
         const uint8_t* st = ring[kb & 1];
         const uint8_t* sta = st + TSA + 128 * wm * 128;
         const uint8_t* stb = st + TSB + 64 * wn * 128;
@@ -252,47 +249,54 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         v8i bfr[4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) bfr[ni] = frag(stb + ni * 2048);
+        // the activation fragment of subtile mi+1 (and its scales) is read
+        // from LDS while the MFMAs of subtile mi run; each subtile's four MFMAs
+        // are issued before their partials are folded into the accumulators
+        const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + sa_off;
+        v8i afn = frag(sta);
         if constexpr (MX) {
             int eb[4];
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) eb[ni] = e8m0_of(scw[64 * wn + 16 * ni + frow]);
+            float san = sca[128 * wm + frow];
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = frag(sta + mi * 2048);
-                const int ea = e8m0_of(sca[128 * wm + 16 * mi + frow]);
+                const v8i af = afn;
+                const int ea = e8m0_of(san);
+                if (mi < 7) {
+                    afn = frag(sta + (mi + 1) * 2048);
+                    san = sca[128 * wm + 16 * (mi + 1) + frow];
+                }
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
             }
-        } else if constexpr (W1) {
+        } else {
             float swv[4];
+            if constexpr (W1) {
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
+                for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
+            } else {
+                const float sws = scw[64 * wn];  // one weight scale per 64-column span
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) swv[ni] = sws;
+            }
+            float4 tn = *reinterpret_cast<const float4*>(sab);
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = frag(sta + mi * 2048);
-                const float4 t4 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(sca) + sa_off + 64 * mi);
-                const float sa4[4] = {t4.x, t4.y, t4.z, t4.w};
+                const v8i af = afn;
+                const float sa4[4] = {tn.x, tn.y, tn.z, tn.w};
+                if (mi < 7) {
+                    afn = frag(sta + (mi + 1) * 2048);
+                    tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
+                }
+                v4f pp[4];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const v4f pp = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int ni = 0; ni < 4; ++ni) pp[ni] = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc[mi][ni][i] = __builtin_fmaf(pp[i], sa4[i] * swv[ni], acc[mi][ni][i]);
-                }
-            }
-        } else {
-            const float sws = scw[64 * wn];  // one weight scale per 64-column span
-#pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = frag(sta + mi * 2048);
-                const float4 t4 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(sca) + sa_off + 64 * mi);
-                const float cmb[4] = {t4.x * sws, t4.y * sws, t4.z * sws, t4.w * sws};
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const v4f pp = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[mi][ni][i] = __builtin_fmaf(pp[i], cmb[i], acc[mi][ni][i]);
-                }
+                        acc[mi][ni][i] = __builtin_fmaf(pp[ni][i], sa4[i] * swv[ni], acc[mi][ni][i]);
             }
         }
     }
@@ -317,65 +321,71 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 // Workgroup tile: one group, 64 tokens x 64 columns, the whole K.  Each
 // K-block is one pipeline stage in LDS: the 64x128-byte activation slab, the
 // 64x128-byte weight slab and the block's scales, all copied by the DMA form
-// of the global loads (global_load_lds: no staging registers).  DNS stages
-// form a ring, DNS-1 of them in flight; one s_waitcnt + barrier per K-block.
-// Every wave issues the same five copies per stage (1 KiB x 2 activation rows
-// groups, 1 KiB x 2 weight row groups, one scale gather), so the wait count is
-// a constant.  Rows are 128 bytes with the 16-byte pieces XOR-swizzled by
-// row & 7, which makes the fragment reads conflict-free.
-// Waves split N (wave w owns columns 16w..16w+15): no partial-sum exchange.
+// of the global loads (global_load_lds: no staging registers).  The eight
+// waves form DKS K-groups of four; each K-group walks its share of the
+// K-blocks through its own ring of DNS stages, DNS-1 of them in flight, with
+// one s_waitcnt + barrier per K-block.  In a K-group, waves 0-1 issue the
+// copies (a copy waits at issue while the CU's memory pipeline is full) and
+// waves 2-3 only compute.  Rows are 128 bytes with the 16-byte pieces
+// XOR-swizzled, which makes the fragment reads conflict-free.  For the MFMAs the waves split N (wave w owns columns
+// 16w..16w+15); the K-groups' partial tiles are summed through LDS.
 constexpr int DBM = 64, DBN = 64, DNS = 4, DKS = 2;
-constexpr int DSTAGE = 64 * 128 * 2 + 1024;  // activations + weights + scales
+constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
+constexpr int DVM = 9;  // copy instructions per copying wave per stage
 
 template <bool MX, bool W1>
 __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int kq = tid >> 8;            // K quarter/half handled by this wave group
-    const int wave = (tid >> 6) & 3;    // column group within the tile
+    const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group within the tile
+    const bool copier = wave < 2;
     const int64_t nblocks = p.G * p.mtiles * p.ntiles;
     const int64_t tile = xcd_remap(blockIdx.x, nblocks);
     const int64_t g = tile / (p.mtiles * p.ntiles);
     const int64_t mt = (tile / p.ntiles) % p.mtiles;
     const int64_t nt = tile % p.ntiles;
     const int64_t m0 = mt * DBM, n0 = nt * DBN;
-    // this wave group's K-blocks: [kb0, kb0 + nkb)
+    // this K-group's K-blocks: [kb0, kb0 + nkb)
     const int64_t kb0 = p.KB * kq / DKS;
     const int64_t nkb = p.KB * (kq + 1) / DKS - kb0;
     const int64_t klast = kb0 + (nkb > 0 ? nkb : 1) - 1;
 
-    // ---- per-lane copy sources (the K-block offset is added per stage)
-    const uint8_t* asrc[2];
-    const uint8_t* wsrc[2];
+    // ---- copy plan.  Copying wave c (0-1): activation rows 32c..32c+31 and
+    // weight rows 32c..32c+31 (8 rows of 128 bytes per instruction), and one
+    // scale gather (lanes 0-31: activation scales of tokens 32c+l; lanes
+    // 32-63: weight scales of columns 32c+l-32).  Sources are uniform bases
+    // plus 32-bit lane offsets.
+    const uint8_t* abase = p.a + g * p.sg;
+    const uint8_t* wbase = p.w + g * p.R * p.D;
+    uint32_t off[8];
+    if (copier) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = 16 * wave + 8 * j + (lane >> 3);
-        const int piece = (lane & 7) ^ swz(row);
-        int64_t m = m0 + row;
-        m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
-        asrc[j] = p.a + m * p.st + g * p.sg + piece * 16;
-        int64_t n = n0 + row;
-        n = n < p.R ? n : p.R - 1;
-        wsrc[j] = p.w + (g * p.R + n) * p.D + piece * 16;
+        for (int j = 0; j < 4; ++j) {
+            const int row = 32 * wave + 8 * j + (lane >> 3);
+            const int piece = (lane & 7) ^ swz(row);
+            int64_t m = m0 + row;
+            m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
+            off[j] = (uint32_t)(m * p.st + piece * 16);
+            int64_t n = n0 + row;
+            n = n < p.R ? n : p.R - 1;
+            off[4 + j] = (uint32_t)(n * p.D + piece * 16);
+        }
     }
-    // scale gather: lanes 0-15 activation scales of tokens 16w+l, lanes 16-31
-    // weight scales of columns 16w+l-16; lanes 32-63 repeat them (junk slots)
+    // the scale gather mixes two sources across lanes: 64-bit lane addresses
     const float* ssrc;
     int64_t sstep;
-    {
-        const int l = lane & 31;
-        if (l < 16) {
-            int64_t m = m0 + 16 * wave + l;
-            m = m < p.T ? m : p.T - 1;
-            ssrc = p.sa + m * p.sst + g * p.ssg;
-            sstep = p.sskb;
-        } else {
-            int64_t n = n0 + 16 * wave + (l - 16);
-            n = n < p.R ? n : p.R - 1;
-            ssrc = p.sw + wscale_index(p, g * p.R + n, 0);
-            sstep = 1;
-        }
+    if (lane < 32) {
+        int64_t m = m0 + 32 * (wave & 1) + lane;
+        m = m < p.T ? m : p.T - 1;
+        ssrc = p.sa + m * p.sst + g * p.ssg;
+        sstep = p.sskb;
+    } else {
+        int64_t n = n0 + 32 * (wave & 1) + (lane - 32);
+        n = n < p.R ? n : p.R - 1;
+        ssrc = p.sw + wscale_index(p, g * p.R + n, 0);
+        sstep = 1;
     }
     const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
     auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
@@ -383,15 +393,16 @@ __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
         kb = kb < klast ? kb : klast;  // tail stages re-copy the last block into a dead slot
         const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            dma16(asrc[j] + kb * 128, st + (16 * wave + 8 * j) * 128);
-            dma16(wsrc[j] + kb * 128, st + 8192 + (16 * wave + 8 * j) * 128);
-        }
+        for (int j = 0; j < 4; ++j) dma16s(abase + kb * 128, off[j], st + (32 * wave + 8 * j) * 128);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16s(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
         dma4(ssrc + kb * sstep, st + 16384 + 256 * wave);
     };
 
+    if (copier) {
 #pragma unroll
-    for (int s = 0; s < DNS - 1; ++s) issue(s, s);
+        for (int s = 0; s < DNS - 1; ++s) issue(s, s);
+    }
 
     v4f acc[4];
 #pragma unroll
@@ -401,10 +412,11 @@ __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
     const int p0 = 2 * (lane >> 4);
     const int64_t nstages = p.KB / DKS + 1;  // >= nkb for every group: same barrier count
     for (int64_t i = 0; i < nstages; ++i) {
-        wait_vmcnt<5 * (DNS - 2)>();  // this wave's copies of stage i have landed
-        __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence: the
-                                       // prefetches stay in flight)
-        issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
+        // this wave's copies of stage i have landed (later stages' copies may
+        // still be in flight)
+        if (copier) wait_vmcnt<DVM * (DNS - 2)>();
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence)
+        if (copier) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
         if (i >= nkb) continue;        // uniform per wave group
         const uint8_t* st = ring[kq][i % DNS];
         v8i bfr;
@@ -415,7 +427,9 @@ __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
             bfr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
         const float* sc = reinterpret_cast<const float*>(st + 16384);
-        const float swv = sc[64 * wave + 16 + (W1 || MX ? frow : 0)];
+        // scales: [64 * c + t] activation scale of token 32c + t, [64 * c + 32 + j]
+        // weight scale of column 32c + j (c = copying wave)
+        const float swv = sc[64 * (wave >> 1) + 32 + 16 * (wave & 1) + (W1 || MX ? frow : 0)];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int r = 16 * mi + frow;
@@ -423,9 +437,11 @@ __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
             const uint4 hi = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
             const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             if constexpr (MX) {
-                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], e8m0_of(sc[64 * mi + frow]), e8m0_of(swv));
+                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], e8m0_of(sc[64 * (mi >> 1) + 16 * (mi & 1) + frow]),
+                                      e8m0_of(swv));
             } else {
-                const float4 t4 = *reinterpret_cast<const float4*>(&sc[64 * mi + 4 * (lane >> 4)]);
+                const float4 t4 =
+                    *reinterpret_cast<const float4*>(&sc[64 * (mi >> 1) + 16 * (mi & 1) + 4 * (lane >> 4)]);
                 const float cmb[4] = {t4.x * swv, t4.y * swv, t4.z * swv, t4.w * swv};
                 const v4f pp = mfma_fp8(af, bfr, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
