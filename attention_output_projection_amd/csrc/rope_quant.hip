@@ -19,7 +19,15 @@
 //     r = 1/s, both IEEE), then broadcast back over the row;
 //   * codes: q = v/s via r and one correction step (exact quotient), clamp to
 //     +-448, hardware e4m3fn conversion; 8 bytes per lane per head.
-// The kernel is HBM-bound: read 1 KiB + write 512 B per head row.
+// Items are numbered in address order (chunk fastest, then group, then
+// token) and dealt round-robin over all waves of the grid, so at any moment
+// the grid reads one compact window of the input (DRAM pages stay open).
+// Each wave loads the next item (head rows, position, table row) while it
+// works on the current one.  The input rows and the codes are streamed with
+// non-temporal loads and stores (each byte is touched once here).  The
+// kernel is HBM-bound: read 1 KiB + write 512 B per head row; a moderate
+// population of waves (12 per CU) keeps enough in flight without crowding
+// the memory controllers.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -30,6 +38,8 @@ namespace oproj {
 namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct RQParams {
     const uint16_t* o;
@@ -39,40 +49,76 @@ struct RQParams {
     float* scales;
     int64_t T, H, hpg, max_pos, nitems;
     int64_t st, sg, sst, ssg, sskb;
-    int nchunk, ipw, pow2;
+    int nchunk, pow2;
 };
 
 template <int CH>
 __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane >> 4;  // quantisation block within the head
     const int li = lane & 15;
-    const int64_t base = (int64_t)blockIdx.x * (kWaves * p.ipw);
+    const int64_t G = p.H / p.hpg;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int64_t first = (int64_t)blockIdx.x * kWaves + wave;  // this wave's item k is first + k*nwaves
+    if (first >= p.nitems) return;
 
-    for (int k = 0; k < p.ipw; ++k) {
-        const int64_t item = base + (int64_t)k * kWaves + wave;
-        if (item >= p.nitems) break;  // wave-uniform
-        const int64_t t = item % p.T;
-        const int64_t rest = item / p.T;
-        const int64_t chunk = rest % p.nchunk;
-        const int64_t g = rest / p.nchunk;
-        const int64_t head0 = g * p.hpg + chunk * CH;
-
-        // ---- loads: CH head rows of 1 KiB, 16 bytes per lane each
-        const uint16_t* src = p.o + (t * p.H + head0) * 512 + 8 * lane;
-        uint4 raw[CH];
+    // item -> (token, group, chunk); items past the end load the last item
+    // (kept in bounds) and are never stored
+    auto split = [&](int64_t item, int64_t& t, int64_t& g, int64_t& chunk) __attribute__((always_inline)) {
+        item = item < p.nitems ? item : p.nitems - 1;
+        chunk = item % p.nchunk;
+        const int64_t rest = item / p.nchunk;
+        g = rest % G;
+        t = rest / G;
+    };
+    auto load_rows = [&](int64_t t, int64_t g, int64_t chunk, uint4* raw) __attribute__((always_inline)) {
+        const uint16_t* src = p.o + (t * p.H + g * p.hpg + chunk * CH) * 512 + 8 * lane;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) raw[j] = *reinterpret_cast<const uint4*>(src + (int64_t)j * 512);
-
-        const int64_t ps = p.pos[t];
+        for (int j = 0; j < CH; ++j) {
+            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
+            raw[j] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+    };
+    auto load_table = [&](int64_t ps, float4& cs, float4& sn) __attribute__((always_inline)) {
         const bool bad = (ps < 0) | (ps >= p.max_pos);
-        float4 cs = make_float4(1.f, 1.f, 1.f, 1.f), sn = make_float4(0.f, 0.f, 0.f, 0.f);
+        cs = make_float4(1.f, 1.f, 1.f, 1.f);
+        sn = make_float4(0.f, 0.f, 0.f, 0.f);
         if (lane >= 56 && !bad) {
             const float* row = p.table + ps * 64 + 4 * (lane - 56);
             cs = *reinterpret_cast<const float4*>(row);
             sn = *reinterpret_cast<const float4*>(row + 32);
         }
+    };
+
+    // pipeline: rows and table row of item k+1 and the position of item k+2
+    // are in flight while item k is processed
+    int64_t tn, gn, cn;
+    split(first, tn, gn, cn);
+    uint4 rawn[CH];
+    load_rows(tn, gn, cn, rawn);
+    int64_t psn = p.pos[tn];
+    float4 csn, snn;
+    load_table(psn, csn, snn);
+    int64_t t2, g2, c2;
+    split(first + nwaves, t2, g2, c2);
+    int64_t ps2 = p.pos[t2];
+
+    for (int64_t item = first; item < p.nitems; item += nwaves) {
+        const int64_t t = tn, g = gn, chunk = cn, ps = psn;
+        uint4 raw[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) raw[j] = rawn[j];
+        const float4 cs = csn, sn = snn;
+        // prefetch item + nwaves (its position is already here) and the
+        // position of item + 2*nwaves
+        tn = t2, gn = g2, cn = c2, psn = ps2;
+        load_rows(tn, gn, cn, rawn);
+        load_table(psn, csn, snn);
+        split(item + 2 * nwaves, t2, g2, c2);
+        ps2 = p.pos[t2];
+
+        const bool bad = (ps < 0) | (ps >= p.max_pos);
 
         // ---- unpack, rotate the RoPE lanes, per-lane |v| max
         float v[CH][8];
@@ -133,7 +179,10 @@ __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p)
             w0 = cvt2_fp8<true>(q[2], q[3], w0);
             uint32_t w1 = cvt2_fp8<false>(q[4], q[5], 0u);
             w1 = cvt2_fp8<true>(q[6], q[7], w1);
-            *reinterpret_cast<uint2*>(dst + (int64_t)j * 512) = make_uint2(w0, w1);
+            u32x2 x;
+            x.x = w0;
+            x.y = w1;
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(dst + (int64_t)j * 512));
         }
     }
 }
@@ -178,8 +227,17 @@ __global__ __launch_bounds__(kWqThreads) void quantize_weight_kernel(const float
 
 }  // namespace
 
+#ifndef OPROJ_Q_CH
+#define OPROJ_Q_CH 4
+#endif
+#ifndef OPROJ_Q_WAVES_PER_CU
+#define OPROJ_Q_WAVES_PER_CU 12
+#endif
+
 hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
-    const int ch = (a.hpg % 8 == 0) ? 8 : (int)a.hpg;  // 1, 2, 4 or 8
+    // heads per item: OPROJ_Q_CH (4 KiB of input per wave per item) when the
+    // group size allows, else the whole group
+    const int ch = (a.hpg % OPROJ_Q_CH == 0) ? OPROJ_Q_CH : (int)a.hpg;  // 1, 2, 4 or 8
     RQParams p;
     p.o = a.o;
     p.pos = a.positions;
@@ -198,12 +256,11 @@ hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
     p.ssg = a.lay.s_stride_g;
     p.sskb = a.lay.s_stride_kb;
     p.pow2 = a.pow2;
-    // items per wave: enough workgroups to fill 256 CUs several times over
-    int64_t ipw = p.nitems / (256 * 8 * kWaves);
-    ipw = ipw < 1 ? 1 : (ipw > 16 ? 16 : ipw);
-    p.ipw = (int)ipw;
-    const int64_t per_block = kWaves * ipw;
-    const dim3 grid((unsigned)((p.nitems + per_block - 1) / per_block));
+    // a fixed population of waves (OPROJ_Q_WAVES_PER_CU per CU on 256 CUs)
+    // walks the items; small batches get one wave per item
+    int64_t waves = 256 * OPROJ_Q_WAVES_PER_CU;
+    if (p.nitems < waves) waves = p.nitems;
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kWaves * 64);
     switch (ch) {
         case 1: hipLaunchKernelGGL(inv_rope_quant_kernel<1>, grid, block, 0, stream, p); break;
