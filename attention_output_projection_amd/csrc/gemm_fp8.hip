@@ -37,6 +37,10 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#ifndef OPROJ_DEC_W_NT
+#define OPROJ_DEC_W_NT 1
+#endif
+
 namespace oproj {
 
 namespace {
@@ -128,6 +132,14 @@ __device__ __forceinline__ uint64_t uniform64(const void* p) {
 }
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(uniform64(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+// Same copy with the non-temporal hint, for data read exactly once (the
+// weight stream of the decode kernel).
+__device__ __forceinline__ void dma16s_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
                  : "v"(voff), "s"(uniform64(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
@@ -395,7 +407,12 @@ __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16s(abase + kb * 128, off[j], st + (32 * wave + 8 * j) * 128);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16s(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
+        for (int j = 0; j < 4; ++j) {
+            if (OPROJ_DEC_W_NT)
+                dma16s_nt(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
+            else
+                dma16s(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
+        }
         dma4(ssrc + kb * sstep, st + 16384 + 256 * wave);
     };
 

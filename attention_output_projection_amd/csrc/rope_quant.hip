@@ -52,7 +52,7 @@ struct RQParams {
     int nchunk, pow2;
 };
 
-template <int CH>
+template <int CH, bool PIPE>
 __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -91,33 +91,9 @@ __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p)
         }
     };
 
-    // pipeline: rows and table row of item k+1 and the position of item k+2
-    // are in flight while item k is processed
-    int64_t tn, gn, cn;
-    split(first, tn, gn, cn);
-    uint4 rawn[CH];
-    load_rows(tn, gn, cn, rawn);
-    int64_t psn = p.pos[tn];
-    float4 csn, snn;
-    load_table(psn, csn, snn);
-    int64_t t2, g2, c2;
-    split(first + nwaves, t2, g2, c2);
-    int64_t ps2 = p.pos[t2];
-
-    for (int64_t item = first; item < p.nitems; item += nwaves) {
-        const int64_t t = tn, g = gn, chunk = cn, ps = psn;
-        uint4 raw[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) raw[j] = rawn[j];
-        const float4 cs = csn, sn = snn;
-        // prefetch item + nwaves (its position is already here) and the
-        // position of item + 2*nwaves
-        tn = t2, gn = g2, cn = c2, psn = ps2;
-        load_rows(tn, gn, cn, rawn);
-        load_table(psn, csn, snn);
-        split(item + 2 * nwaves, t2, g2, c2);
-        ps2 = p.pos[t2];
-
+    // rotate, reduce, scale, convert and store one item
+    auto process = [&](int64_t t, int64_t g, int64_t chunk, int64_t ps, const uint4* raw, float4 cs,
+                       float4 sn) __attribute__((always_inline)) {
         const bool bad = (ps < 0) | (ps >= p.max_pos);
 
         // ---- unpack, rotate the RoPE lanes, per-lane |v| max
@@ -184,6 +160,40 @@ __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p)
             x.y = w1;
             __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(dst + (int64_t)j * 512));
         }
+    };
+
+    int64_t tn, gn, cn;
+    split(first, tn, gn, cn);
+    uint4 rawn[CH];
+    load_rows(tn, gn, cn, rawn);
+    int64_t psn = p.pos[tn];
+    float4 csn, snn;
+    load_table(psn, csn, snn);
+    if constexpr (!PIPE) {  // one item per wave (small batches): no pipeline
+        process(tn, gn, cn, psn, rawn, csn, snn);
+        return;
+    }
+
+    // pipeline: rows and table row of item k+1 and the position of item k+2
+    // are in flight while item k is processed
+    int64_t t2, g2, c2;
+    split(first + nwaves, t2, g2, c2);
+    int64_t ps2 = p.pos[t2];
+
+    for (int64_t item = first; item < p.nitems; item += nwaves) {
+        const int64_t t = tn, g = gn, chunk = cn, ps = psn;
+        uint4 raw[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) raw[j] = rawn[j];
+        const float4 cs = csn, sn = snn;
+        // prefetch item + nwaves (its position is already here) and the
+        // position of item + 2*nwaves
+        tn = t2, gn = g2, cn = c2, psn = ps2;
+        load_rows(tn, gn, cn, rawn);
+        load_table(psn, csn, snn);
+        split(item + 2 * nwaves, t2, g2, c2);
+        ps2 = p.pos[t2];
+        process(t, g, chunk, ps, raw, cs, sn);
     }
 }
 
@@ -262,12 +272,19 @@ hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
     if (p.nitems < waves) waves = p.nitems;
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kWaves * 64);
+    const bool pipe = p.nitems > waves;  // else every wave takes exactly one item
+#define OPROJ_RQ_LAUNCH(C)                                                                    \
+    if (pipe)                                                                                 \
+        hipLaunchKernelGGL((inv_rope_quant_kernel<C, true>), grid, block, 0, stream, p);      \
+    else                                                                                      \
+        hipLaunchKernelGGL((inv_rope_quant_kernel<C, false>), grid, block, 0, stream, p);
     switch (ch) {
-        case 1: hipLaunchKernelGGL(inv_rope_quant_kernel<1>, grid, block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL(inv_rope_quant_kernel<2>, grid, block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL(inv_rope_quant_kernel<4>, grid, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL(inv_rope_quant_kernel<8>, grid, block, 0, stream, p); break;
+        case 1: OPROJ_RQ_LAUNCH(1) break;
+        case 2: OPROJ_RQ_LAUNCH(2) break;
+        case 4: OPROJ_RQ_LAUNCH(4) break;
+        default: OPROJ_RQ_LAUNCH(8) break;
     }
+#undef OPROJ_RQ_LAUNCH
     return hipGetLastError();
 }
 
