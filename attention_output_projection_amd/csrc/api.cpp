@@ -156,6 +156,9 @@ oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, co
 oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* x, const void* w,
                                    void* y, void* stream) {
     if (M < 0 || N < 1 || K < 64 || K % 64 != 0 || N % 16 != 0) return OPROJ_E_SHAPE;
+    // the kernel addresses each operand as a uniform base plus 32-bit lane offsets
+    const int64_t lim = (int64_t)1 << 32;
+    if (M * K * 2 > lim || N * K * 2 > lim) return OPROJ_E_SHAPE;
     if (M == 0) return OPROJ_OK;
     if (!x || !w || !y) return OPROJ_E_NULL;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return OPROJ_E_ALIGN;

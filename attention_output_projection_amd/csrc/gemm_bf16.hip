@@ -1,21 +1,33 @@
 // gemm_bf16.hip -- step a4 on gfx950: the dense wo_b GEMM over the flattened
 // z (sglang source page "python/sglang/srt/models/deepseek_v4.py",
 // MQALayer.forward: wo_b is applied to z.flatten(1); wo_b is a linear layer
-// from G*R to hidden, weight [hidden, G*R]):
+// from G*R to hidden, weight [hidden, G*R]; vLLM API page
+// "vllm.models.deepseek_v4.nvidia.ops.o_proj", deep_gemm_fp8_o_proj ends with
+// wo_b(z.flatten(1))):
 //   y[m][j] = sum_c x[m][c] * w[j][c],  bf16 in, fp32 accumulate, bf16 out.
 //
-// v_mfma_f32_16x16x32_bf16, 128x128 output tile per 256-thread workgroup
-// (2x2 waves of 64x64), K staged 64 deep (128 bytes per row) through
-// double-buffered LDS with rows padded to 144 bytes; the accumulators stay in
-// the matrix-core result registers for the whole K loop.
+// Same pipeline as the FP8 tile kernel: 256x256 output tile per 512-thread
+// workgroup, eight waves as 2 (M) x 4 (N) of 128x64, one 64-deep K-step (128
+// bytes of every row) per stage, stages double-buffered in LDS (2 x 64 KiB)
+// and filled by DMA copies (global_load_lds) into XOR-swizzled 128-byte rows.
+// Waves 0-3 issue the copies, waves 4-7 only compute.  MFMA
+// v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a row (pieces 2q
+// and 2q+1 for lane group q) feed the two K=32 halves of the step, in the same
+// order for both operands, so the pair of MFMAs sums the whole 64-deep step.
+// The accumulators stay in the matrix-core result registers for the whole K
+// loop.  Tiles are walked in bands of four M-tiles (the N-tiles of a band share
+// its activation rows) and consecutive tiles are kept on one XCD.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace oproj {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BKB = 128 /* bytes of K per stage */, LROW = 144;
+constexpr int BM = 256, BN = 256, NW = 8;
+constexpr int SA = 0, SB = BM * 128, STAGE = SB + BN * 128;  // 65536 bytes
+constexpr int BAND = 4;  // M-tiles per band of the tile order
 
 struct DParams {
     const uint16_t* x;
@@ -30,89 +42,113 @@ __device__ __forceinline__ int64_t xcd_remap_d(int64_t bid, int64_t nblocks) {
     return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(DParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * LROW];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LROW];
+__global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[2][STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+    const int wm = wave & 1, wn = wave >> 1;
     const int64_t nblocks = p.mtiles * p.ntiles;
-    const int64_t tile = xcd_remap_d(blockIdx.x, nblocks);
-    const int64_t mt = tile / p.ntiles, nt = tile % p.ntiles;
+    const int64_t id = xcd_remap_d(blockIdx.x, nblocks);
+    // band order: BAND M-tiles x all N-tiles, M fastest within the band
+    const int64_t band = id / (BAND * p.ntiles);
+    const int64_t mfirst = band * BAND;
+    const int64_t bh = (p.mtiles - mfirst) < BAND ? (p.mtiles - mfirst) : BAND;
+    const int64_t local = id - band * BAND * p.ntiles;
+    const int64_t mt = mfirst + local % bh, nt = local / bh;
     const int64_t m0 = mt * BM, n0 = nt * BN;
     const int64_t kbytes = p.K * 2;
-    const int64_t nstage = kbytes / BKB;
+    const int64_t nstage = kbytes / 128;
 
-    const int crow = tid >> 3;
-    const int ccol = (tid & 7) * 16;
-    const uint8_t* aptr[4];
-    const uint8_t* bptr[4];
+    // ---- copy plan: copying wave c (0-3) moves activation rows 64c..64c+63
+    // and weight rows 64c..64c+63, 8 rows of 128 bytes per instruction;
+    // sources are uniform bases plus 32-bit lane offsets (the host keeps every
+    // offset below 2^32)
+    const bool copier = wave < 4;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x);
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.w);
+    uint32_t off[16];
+    if (copier) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t m = m0 + crow + 32 * i;
-        m = m < p.M ? m : p.M - 1;
-        aptr[i] = reinterpret_cast<const uint8_t*>(p.x) + m * kbytes + ccol;
-        int64_t n = n0 + crow + 32 * i;
-        n = n < p.N ? n : p.N - 1;
-        bptr[i] = reinterpret_cast<const uint8_t*>(p.w) + n * kbytes + ccol;
+        for (int j = 0; j < 8; ++j) {
+            const int row = 64 * wave + 8 * j + (lane >> 3);
+            const int piece = (lane & 7) ^ swz(row);
+            int64_t m = m0 + row;
+            m = m < p.M ? m : p.M - 1;  // rows past M are computed but never stored
+            off[j] = (uint32_t)(m * kbytes + piece * 16);
+            int64_t n = n0 + row;
+            n = n < p.N ? n : p.N - 1;
+            off[8 + j] = (uint32_t)(n * kbytes + piece * 16);
+        }
     }
-    uint4 ra[4], rb[4];
-#define OPROJ_GLOAD(ks)                                                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                \
-        ra[i] = *reinterpret_cast<const uint4*>(aptr[i] + (ks) * BKB);             \
-        rb[i] = *reinterpret_cast<const uint4*>(bptr[i] + (ks) * BKB);             \
-    }
-#define OPROJ_SWRITE(buf)                                                          \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                \
-        *reinterpret_cast<uint4*>(&sA[buf][(crow + 32 * i) * LROW + ccol]) = ra[i]; \
-        *reinterpret_cast<uint4*>(&sB[buf][(crow + 32 * i) * LROW + ccol]) = rb[i]; \
-    }
+    const uint32_t ring0 = lds_offset(&ring[0][0]);
+    const uint32_t adst = ring0 + SA + 64 * (wave & 3) * 128, bdst = ring0 + SB + 64 * (wave & 3) * 128;
+    auto issue = [&](int64_t ks, int slot) __attribute__((always_inline)) {
+        ks = ks < nstage ? ks : nstage - 1;  // past the end: re-copy the last step into a dead slot
+        const uint32_t so = (uint32_t)(slot * STAGE);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16s(xb + ks * 128, off[j], adst + so + j * 1024);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16s(wb + ks * 128, off[8 + j], bdst + so + j * 1024);
+    };
+    if (copier) issue(0, 0);
 
-    v4f acc[4][4];
+    v4f acc[8][4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // fragment addressing: rows 16k + frow share the swizzle of frow
     const int frow = lane & 15;
-    const int fk = (lane >> 4) * 16;
+    const int p0 = 2 * (lane >> 4);
+    const int lo_off = frow * 128 + 16 * (p0 ^ swz(frow));
+    const int hi_off = frow * 128 + 16 * ((p0 + 1) ^ swz(frow));
+    auto ld = [&](const uint8_t* base, int o) __attribute__((always_inline)) {
+        return *reinterpret_cast<const v8bf*>(base + o);
+    };
 
-    OPROJ_GLOAD(0);
-    OPROJ_SWRITE(0);
-    __syncthreads();
     for (int64_t ks = 0; ks < nstage; ++ks) {
-        const int buf = (int)(ks & 1);
-        // unconditional (clamped) prefetch keeps the staging registers out of scratch
-        OPROJ_GLOAD(ks + 1 < nstage ? ks + 1 : ks);
+        if (copier) wait_vmcnt<0>();   // this wave's copies of step ks have landed
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's; step ks-1 is free
+        if (copier) issue(ks + 1, (int)((ks + 1) & 1));
+        const uint8_t* st = ring[ks & 1];
+        const uint8_t* sta = st + SA + 128 * wm * 128;
+        const uint8_t* stb = st + SB + 64 * wn * 128;
+        v8bf blo[4], bhi[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v8bf af[4], bfr[4];
+        for (int ni = 0; ni < 4; ++ni) {
+            blo[ni] = ld(stb + ni * 2048, lo_off);
+            bhi[ni] = ld(stb + ni * 2048, hi_off);
+        }
+        // activation fragments of subtile mi+1 are read while subtile mi runs
+        v8bf alo = ld(sta, lo_off), ahi = ld(sta, hi_off);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = *reinterpret_cast<const v8bf*>(&sA[buf][(wm * 64 + mi * 16 + frow) * LROW + h * 64 + fk]);
+        for (int mi = 0; mi < 8; ++mi) {
+            const v8bf a0 = alo, a1 = ahi;
+            if (mi < 7) {
+                alo = ld(sta + (mi + 1) * 2048, lo_off);
+                ahi = ld(sta + (mi + 1) * 2048, hi_off);
+            }
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-                bfr[ni] = *reinterpret_cast<const v8bf*>(&sB[buf][(wn * 64 + ni * 16 + frow) * LROW + h * 64 + fk]);
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, blo[ni], acc[mi][ni], 0, 0, 0);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bhi[ni], acc[mi][ni], 0, 0, 0);
         }
-        if (ks + 1 < nstage) { OPROJ_SWRITE(buf ^ 1); }
-        __syncthreads();
     }
+    wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
 
-#undef OPROJ_GLOAD
-#undef OPROJ_SWRITE
+    // epilogue: bf16 (nearest even)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
-                const int64_t col = n0 + wn * 64 + ni * 16 + frow;
+                const int64_t row = m0 + 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
+                const int64_t col = n0 + 64 * wn + 16 * ni + frow;
                 if (row < p.M && col < p.N) p.y[row * p.N + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
             }
 }
@@ -129,7 +165,7 @@ hipError_t launch_dense_bf16_gemm(const DenseGemmArgs& a, hipStream_t stream) {
     p.K = a.K;
     p.mtiles = (a.M + BM - 1) / BM;
     p.ntiles = (a.N + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(p.mtiles * p.ntiles)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(p.mtiles * p.ntiles)), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -138,7 +138,8 @@ oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, co
 /* Step a4 ([SGL] MQALayer.forward applies wo_b to z.flatten(1)):
  *   y[m][j] = sum_c x[m][c] * w[j][c], bf16 inputs, fp32 accumulation, bf16 out.
  *  x  bf16 [M][K] row-major;  w  bf16 [N][K] row-major;  y  bf16 [M][N].
- *  K must be a multiple of 64 and N a multiple of 16. */
+ *  K must be a multiple of 64 and N a multiple of 16; each operand must span
+ *  at most 4 GiB (M*K*2 and N*K*2 bytes), else OPROJ_E_SHAPE. */
 oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* x, const void* w,
                                    void* y, void* stream);
 

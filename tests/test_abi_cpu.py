@@ -107,6 +107,8 @@ def test_dense_gemm_validation(lib):
     assert f(-1, 7168, 16384) == E_SHAPE
     assert f(4, 7168, 100) == E_SHAPE
     assert f(4, 7000, 128) == E_SHAPE  # N % 16 != 0
+    assert f(1 << 17, 16, 1 << 15) == E_SHAPE  # activation operand beyond 4 GiB
+    assert f(4, 1 << 17, 1 << 15) == E_SHAPE  # weight operand beyond 4 GiB
     assert f(4, 16, 64, x=None) == E_NULL
     assert f(4, 16, 64, y=BAD) == E_ALIGN
 

@@ -322,6 +322,19 @@ def test_dense_bf16_gemm_parity():
     assert e <= TOL, e
 
 
+@pytest.mark.parametrize("M,N,K", [(600, 1040, 192), (1, 16, 64), (257, 272, 128), (513, 784, 320)])
+def test_dense_bf16_gemm_ragged(M, N, K):
+    """Several 256x256 tiles with ragged M and N tails and odd step counts, checked densely."""
+    x = wl.bf16_matrix(wl.seed_of(92, M), M, K, 1.0)
+    wb = wl.bf16_matrix(wl.seed_of(93, N), N, K, 0.02)
+    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ap.oproj_dense_bf16_gemm(M, N, K, _dev(x.view(np.int16)), _dev(wb.view(np.int16)), y)
+    yg = U.bf16_bits_to_f64(_host(y).view(np.uint16))
+    ref = oracle.dense_gemm_bf16(x, wb)
+    e = U.rel_max_err(yg, ref)
+    assert e <= TOL, e
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode"])
 def test_fused_equals_steps(name):
     w = wl.WORKLOADS[name]
