@@ -86,10 +86,12 @@ const char* oproj_status_string(oproj_status s) {
 
 const char* oproj_version(void) { return "0.1.0"; }
 
-oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
-                                  const int64_t* positions, const float* cos_sin, void* a_codes,
-                                  float* a_scales, const oproj_act_layout* out_layout,
-                                  void* stream) {
+namespace {
+
+// Validation + argument set-up of step a1+a2 (shared by the entry points).
+oproj_status prep_quant(const oproj_shape* shape, int32_t scale_mode, const void* o, const int64_t* positions,
+                        const float* cos_sin, void* a_codes, float* a_scales, const oproj_act_layout* out_layout,
+                        oproj::RopeQuantArgs* a) {
     oproj_status st = check_shape(shape, false);
     if (st != OPROJ_OK) return st;
     if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
@@ -99,25 +101,24 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
     if (!aligned16(o) || !aligned16(cos_sin) || !aligned16(a_codes) ||
         (reinterpret_cast<uintptr_t>(positions) & 7u) || (reinterpret_cast<uintptr_t>(a_scales) & 3u))
         return OPROJ_E_ALIGN;
-    oproj::RopeQuantArgs a;
-    a.T = shape->T;
-    a.G = shape->n_groups;
-    a.hpg = shape->heads_per_group;
-    a.max_pos = shape->max_pos;
-    a.pow2 = scale_mode == OPROJ_SCALE_POW2;
-    a.o = static_cast<const uint16_t*>(o);
-    a.positions = positions;
-    a.cos_sin = cos_sin;
-    a.codes = static_cast<uint8_t*>(a_codes);
-    a.scales = a_scales;
-    a.lay = to_layout(out_layout, shape);
-    return from_hip(oproj::launch_inv_rope_quant(a, static_cast<hipStream_t>(stream)));
+    a->T = shape->T;
+    a->G = shape->n_groups;
+    a->hpg = shape->heads_per_group;
+    a->max_pos = shape->max_pos;
+    a->pow2 = scale_mode == OPROJ_SCALE_POW2;
+    a->o = static_cast<const uint16_t*>(o);
+    a->positions = positions;
+    a->cos_sin = cos_sin;
+    a->codes = static_cast<uint8_t*>(a_codes);
+    a->scales = a_scales;
+    a->lay = to_layout(out_layout, shape);
+    return OPROJ_OK;
 }
 
-oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
-                                const float* a_scales, const oproj_act_layout* a_layout,
-                                const void* w_codes, const float* w_scales, int32_t w_block,
-                                void* z, void* stream) {
+// Validation + argument set-up of step a3 (shared by the entry points).
+oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void* a_codes, const float* a_scales,
+                       const oproj_act_layout* a_layout, const void* w_codes, const float* w_scales,
+                       int32_t w_block, void* z, oproj::GroupedGemmArgs* a) {
     oproj_status st = check_shape(shape, true);
     if (st != OPROJ_OK) return st;
     if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
@@ -137,19 +138,41 @@ oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, co
             rows * D >= lim || rows * KB * 4 >= lim)
             return OPROJ_E_SHAPE;
     }
+    a->T = shape->T;
+    a->G = shape->n_groups;
+    a->D = shape->heads_per_group * 512;
+    a->R = shape->o_lora_rank;
+    a->mx = scale_mode == OPROJ_SCALE_POW2;
+    a->w_1x128 = w_block == OPROJ_WBLOCK_1x128;
+    a->a = static_cast<const uint8_t*>(a_codes);
+    a->sa = a_scales;
+    a->lay = to_layout(a_layout, shape);
+    a->w = static_cast<const uint8_t*>(w_codes);
+    a->sw = w_scales;
+    a->z = static_cast<uint16_t*>(z);
+    return OPROJ_OK;
+}
+
+}  // namespace
+
+oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                                  const int64_t* positions, const float* cos_sin, void* a_codes,
+                                  float* a_scales, const oproj_act_layout* out_layout,
+                                  void* stream) {
+    oproj::RopeQuantArgs a;
+    const oproj_status st = prep_quant(shape, scale_mode, o, positions, cos_sin, a_codes, a_scales, out_layout, &a);
+    if (st != OPROJ_OK || shape->T == 0) return st;
+    return from_hip(oproj::launch_inv_rope_quant(a, static_cast<hipStream_t>(stream)));
+}
+
+oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
+                                const float* a_scales, const oproj_act_layout* a_layout,
+                                const void* w_codes, const float* w_scales, int32_t w_block,
+                                void* z, void* stream) {
     oproj::GroupedGemmArgs a;
-    a.T = shape->T;
-    a.G = shape->n_groups;
-    a.D = shape->heads_per_group * 512;
-    a.R = shape->o_lora_rank;
-    a.mx = scale_mode == OPROJ_SCALE_POW2;
-    a.w_1x128 = w_block == OPROJ_WBLOCK_1x128;
-    a.a = static_cast<const uint8_t*>(a_codes);
-    a.sa = a_scales;
-    a.lay = to_layout(a_layout, shape);
-    a.w = static_cast<const uint8_t*>(w_codes);
-    a.sw = w_scales;
-    a.z = static_cast<uint16_t*>(z);
+    const oproj_status st =
+        prep_gemm(shape, scale_mode, a_codes, a_scales, a_layout, w_codes, w_scales, w_block, z, &a);
+    if (st != OPROJ_OK || shape->T == 0) return st;
     return from_hip(oproj::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -201,11 +224,22 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
     void* codes = ws;
     float* scales = reinterpret_cast<float*>(ws + round_up(T * G * D));
     void* zbuf = wo_b ? (void*)(ws + round_up(T * G * D) + round_up(T * G * KB * sizeof(float))) : out;
-    st = oproj_inv_rope_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, stream);
-    if (st != OPROJ_OK) return st;
-    st = oproj_grouped_wo_a(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block,
-                            zbuf, stream);
-    if (st != OPROJ_OK || !wo_b) return st;
+    oproj::RopeQuantArgs qa;
+    oproj::GroupedGemmArgs ga;
+    if ((st = prep_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, &qa)) != OPROJ_OK)
+        return st;
+    if ((st = prep_gemm(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block, zbuf, &ga)) !=
+        OPROJ_OK)
+        return st;
+    if (wo_b) {  // validate a4 before anything is enqueued
+        const int64_t K = shape->n_groups * shape->o_lora_rank, lim = int64_t(1) << 32;
+        if (K % 64 != 0 || shape->T * K * 2 > lim || hidden * K * 2 > lim) return OPROJ_E_SHAPE;
+        if (!aligned16(wo_b)) return OPROJ_E_ALIGN;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = from_hip(oproj::launch_inv_rope_quant(qa, s))) != OPROJ_OK) return st;
+    if ((st = from_hip(oproj::launch_grouped_gemm(ga, s))) != OPROJ_OK) return st;
+    if (!wo_b) return OPROJ_OK;
     return oproj_dense_bf16_gemm(shape->T, hidden, shape->n_groups * shape->o_lora_rank, zbuf, wo_b,
                                  out, stream);
 }

@@ -272,10 +272,10 @@ constexpr int DBM = 64, DBN = 64, DNS = 4, DKS = 2;
 constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
 constexpr int DVM = 9;  // copy instructions per copying wave per stage
 
+// One workgroup's output tile (the whole decode pipeline); ring is the
+// workgroup's LDS.
 template <bool MX, bool W1>
-__global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
-
+__device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DKS][DNS][DSTAGE]) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group within the tile
@@ -424,6 +424,12 @@ __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
             const int64_t row = m0 + mi * 16 + 4 * (lane >> 4) + i;
             if (row < p.T && col < p.R) p.z[(row * p.G + g) * p.R + col] = (uint16_t)f32_to_bf16_bits(acc[mi][i]);
         }
+}
+
+template <bool MX, bool W1>
+__global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
+    decode_tile<MX, W1>(p, ring);
 }
 
 void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {

@@ -30,6 +30,7 @@
 // the memory controllers.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "rq_item.hpp"
 
 #pragma clang fp contract(off)
 
@@ -38,146 +39,34 @@ namespace oproj {
 namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-struct RQParams {
-    const uint16_t* o;
-    const int64_t* pos;
-    const float* table;
-    uint8_t* codes;
-    float* scales;
-    int64_t T, H, hpg, max_pos, nitems;
-    int64_t st, sg, sst, ssg, sskb;
-    int nchunk, pow2;
-};
+typedef rq::Params RQParams;
 
 template <int CH, bool PIPE>
 __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane >> 4;  // quantisation block within the head
-    const int li = lane & 15;
-    const int64_t G = p.H / p.hpg;
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t first = (int64_t)blockIdx.x * kWaves + wave;  // this wave's item k is first + k*nwaves
     if (first >= p.nitems) return;
-
-    // item -> (token, group, chunk); items past the end load the last item
-    // (kept in bounds) and are never stored
-    auto split = [&](int64_t item, int64_t& t, int64_t& g, int64_t& chunk) __attribute__((always_inline)) {
-        item = item < p.nitems ? item : p.nitems - 1;
-        chunk = item % p.nchunk;
-        const int64_t rest = item / p.nchunk;
-        g = rest % G;
-        t = rest / G;
-    };
-    auto load_rows = [&](int64_t t, int64_t g, int64_t chunk, uint4* raw) __attribute__((always_inline)) {
-        const uint16_t* src = p.o + (t * p.H + g * p.hpg + chunk * CH) * 512 + 8 * lane;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
-            raw[j] = make_uint4(x.x, x.y, x.z, x.w);
-        }
-    };
-    auto load_table = [&](int64_t ps, float4& cs, float4& sn) __attribute__((always_inline)) {
-        const bool bad = (ps < 0) | (ps >= p.max_pos);
-        cs = make_float4(1.f, 1.f, 1.f, 1.f);
-        sn = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lane >= 56 && !bad) {
-            const float* row = p.table + ps * 64 + 4 * (lane - 56);
-            cs = *reinterpret_cast<const float4*>(row);
-            sn = *reinterpret_cast<const float4*>(row + 32);
-        }
-    };
-
-    // rotate, reduce, scale, convert and store one item
-    auto process = [&](int64_t t, int64_t g, int64_t chunk, int64_t ps, const uint4* raw, float4 cs,
-                       float4 sn) __attribute__((always_inline)) {
-        const bool bad = (ps < 0) | (ps >= p.max_pos);
-
-        // ---- unpack, rotate the RoPE lanes, per-lane |v| max
-        float v[CH][8];
-        float am[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const uint32_t w4[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                v[j][2 * m] = bf16_lo(w4[m]);
-                v[j][2 * m + 1] = bf16_hi(w4[m]);
-            }
-        }
-        if (lane >= 56) {
-            const float cc[4] = {cs.x, cs.y, cs.z, cs.w};
-            const float ss[4] = {sn.x, sn.y, sn.z, sn.w};
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float e = v[j][2 * m], d = v[j][2 * m + 1];
-                    v[j][2 * m] = __builtin_fmaf(d, ss[m], e * cc[m]);
-                    v[j][2 * m + 1] = __builtin_fmaf(-e, ss[m], d * cc[m]);
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            float a = fabsf(v[j][0]);
-#pragma unroll
-            for (int m = 1; m < 8; ++m) a = fmaxf(a, fabsf(v[j][m]));
-            am[j] = row16_max(a);
-        }
-
-        // ---- one scale per (head j, block c), computed by lane 16c + j
-        float asel = am[0];
-#pragma unroll
-        for (int j = 1; j < CH; ++j) asel = ((li % CH) == j) ? am[j] : asel;
-        float s = fmaxf(asel, kAmaxFloor) / kFp8Max;
-        if (p.pow2) s = pow2_ceil(s);
-        if (bad) s = __builtin_nanf("");
-        const float r = 1.0f / s;
-
-        if (li < CH) {
-            const int64_t kb = (chunk * CH + li) * 4 + c;
-            p.scales[t * p.sst + g * p.ssg + kb * p.sskb] = s;
-        }
-
-        uint8_t* dst = p.codes + t * p.st + g * p.sg + chunk * CH * 512 + 8 * lane;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const float sj = __shfl(s, (lane & ~15) + j);
-            const float rj = __shfl(r, (lane & ~15) + j);
-            float q[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) q[m] = div_by_scale(v[j][m], sj, rj);
-            uint32_t w0 = cvt2_fp8<false>(q[0], q[1], 0u);
-            w0 = cvt2_fp8<true>(q[2], q[3], w0);
-            uint32_t w1 = cvt2_fp8<false>(q[4], q[5], 0u);
-            w1 = cvt2_fp8<true>(q[6], q[7], w1);
-            u32x2 x;
-            x.x = w0;
-            x.y = w1;
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(dst + (int64_t)j * 512));
-        }
-    };
+    const rq::Wave<CH> w(p, lane);
 
     int64_t tn, gn, cn;
-    split(first, tn, gn, cn);
+    w.split(first, tn, gn, cn);
     uint4 rawn[CH];
-    load_rows(tn, gn, cn, rawn);
+    w.load_rows(tn, gn, cn, rawn);
     int64_t psn = p.pos[tn];
     float4 csn, snn;
-    load_table(psn, csn, snn);
+    w.load_table(psn, csn, snn);
     if constexpr (!PIPE) {  // one item per wave (small batches): no pipeline
-        process(tn, gn, cn, psn, rawn, csn, snn);
+        w.process(tn, gn, cn, psn, rawn, csn, snn);
         return;
     }
 
     // pipeline: rows and table row of item k+1 and the position of item k+2
     // are in flight while item k is processed
     int64_t t2, g2, c2;
-    split(first + nwaves, t2, g2, c2);
+    w.split(first + nwaves, t2, g2, c2);
     int64_t ps2 = p.pos[t2];
 
     for (int64_t item = first; item < p.nitems; item += nwaves) {
@@ -189,11 +78,11 @@ __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p)
         // prefetch item + nwaves (its position is already here) and the
         // position of item + 2*nwaves
         tn = t2, gn = g2, cn = c2, psn = ps2;
-        load_rows(tn, gn, cn, rawn);
-        load_table(psn, csn, snn);
-        split(item + 2 * nwaves, t2, g2, c2);
+        w.load_rows(tn, gn, cn, rawn);
+        w.load_table(psn, csn, snn);
+        w.split(item + 2 * nwaves, t2, g2, c2);
         ps2 = p.pos[t2];
-        process(t, g, chunk, ps, raw, cs, sn);
+        w.process(t, g, chunk, ps, raw, cs, sn);
     }
 }
 
@@ -237,35 +126,13 @@ __global__ __launch_bounds__(kWqThreads) void quantize_weight_kernel(const float
 
 }  // namespace
 
-#ifndef OPROJ_Q_CH
-#define OPROJ_Q_CH 4
-#endif
 #ifndef OPROJ_Q_WAVES_PER_CU
 #define OPROJ_Q_WAVES_PER_CU 12
 #endif
 
 hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
-    // heads per item: OPROJ_Q_CH (4 KiB of input per wave per item) when the
-    // group size allows, else the whole group
-    const int ch = (a.hpg % OPROJ_Q_CH == 0) ? OPROJ_Q_CH : (int)a.hpg;  // 1, 2, 4 or 8
-    RQParams p;
-    p.o = a.o;
-    p.pos = a.positions;
-    p.table = a.cos_sin;
-    p.codes = a.codes;
-    p.scales = a.scales;
-    p.T = a.T;
-    p.H = a.G * a.hpg;
-    p.hpg = a.hpg;
-    p.max_pos = a.max_pos;
-    p.nchunk = (int)(a.hpg / ch);
-    p.nitems = a.T * a.G * p.nchunk;
-    p.st = a.lay.stride_t;
-    p.sg = a.lay.stride_g;
-    p.sst = a.lay.s_stride_t;
-    p.ssg = a.lay.s_stride_g;
-    p.sskb = a.lay.s_stride_kb;
-    p.pow2 = a.pow2;
+    const int ch = rq::heads_per_item(a.hpg);  // 1, 2 or 4
+    const RQParams p = rq::make_params(a, ch);
     // a fixed population of waves (OPROJ_Q_WAVES_PER_CU per CU on 256 CUs)
     // walks the items; small batches get one wave per item
     int64_t waves = 256 * OPROJ_Q_WAVES_PER_CU;
@@ -281,8 +148,7 @@ hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
     switch (ch) {
         case 1: OPROJ_RQ_LAUNCH(1) break;
         case 2: OPROJ_RQ_LAUNCH(2) break;
-        case 4: OPROJ_RQ_LAUNCH(4) break;
-        default: OPROJ_RQ_LAUNCH(8) break;
+        default: OPROJ_RQ_LAUNCH(4) break;
     }
 #undef OPROJ_RQ_LAUNCH
     return hipGetLastError();

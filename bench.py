@@ -1,9 +1,9 @@
 """Benchmark of the O-projection front half on one MI355X.
 
-One step = one pass of the hot path over one batch of synthetic input:
-inverse RoPE + 1x128 FP8 quantisation (oproj_inv_rope_quant) followed by the
-grouped wo_a GEMM (oproj_grouped_wo_a) -- exactly what oproj_fused enqueues --
-plus the dense wo_b GEMM for the workload that has one.  The default workload
+One step = one pass of the hot path over one batch of synthetic input: one
+oproj_fused call -- inverse RoPE + 1x128 FP8 quantisation, then the grouped
+wo_a GEMM, plus the dense wo_b GEMM for the workload that has one.  The kernels are also timed
+one by one (oproj_inv_rope_quant, oproj_grouped_wo_a, oproj_dense_bf16_gemm).  The default workload
 is the decode batch (T=64, 16 groups x 8 heads, D=4096, R=1024).
 
 Inputs are resident in HBM before timing starts.  The steps rotate through
@@ -58,6 +58,14 @@ def kernel_bytes_gemm(w) -> int:
 
 def kernel_flops_gemm(w) -> int:
     return 2 * w.T * w.n_groups * w.o_lora_rank * w.D
+
+
+# the source files each kernel is built from (the counters are tied to them)
+KERNEL_SOURCES = {
+    "inv_rope_quant": ("rope_quant.hip", "rq_item.hpp", "device_common.hpp"),
+    "grouped_wo_a": ("gemm_fp8.hip", "lds_dma.hpp", "device_common.hpp"),
+    "wo_b": ("gemm_bf16.hip", "lds_dma.hpp", "device_common.hpp"),
+}
 
 
 def source_sha(*names: str) -> str:
@@ -164,6 +172,8 @@ def main() -> int:
     d_w32 = t(wmat)
     wrows = w.n_groups * w.o_lora_rank
     srows = wrows if w.w_block_rows == 1 else (wrows + 127) // 128
+    hidden = w.hidden if wob is not None else 0
+    ws_bytes = ap.oproj_fused_workspace_bytes(shp, hidden)
     C = []
     for i in range(copies):
         c = {}
@@ -177,6 +187,7 @@ def main() -> int:
         if wob is not None:
             c["wob"] = t(wob.view(np.int16))
             c["y"] = torch.empty((w.T, w.hidden), dtype=torch.int16, device=dev)
+        c["work"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         C.append(c)
     del d_w32
     torch.cuda.synchronize()
@@ -190,11 +201,10 @@ def main() -> int:
     def wo_b(c):
         ap.oproj_dense_bf16_gemm(w.T, w.hidden, wrows, c["z"], c["wob"], c["y"])
 
-    def step(c):
-        quant(c)
-        gemm(c)
-        if wob is not None:
-            wo_b(c)
+    def step(c):  # the whole path: one oproj_fused call
+        out = c["y"] if wob is not None else c["z"]
+        ap.oproj_fused(shp, mode, c["o"], d_pos, d_tab, c["wq"], c["ws"], wblock,
+                       c.get("wob"), hidden, c["work"], ws_bytes, out)
 
     # eager reference result of copy 0
     step(C[0])
@@ -285,17 +295,15 @@ def main() -> int:
 
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
     kd = kernels[dominant]
+    sha = source_sha(*KERNEL_SOURCES[dominant])
     if dominant == "inv_rope_quant":
-        sha = source_sha("rope_quant.hip", "device_common.hpp")
         achieved, peak, unit, bound = kd["GB/s"], HBM_PEAK_GBS, "GB/s", "hbm"
     elif dominant == "grouped_wo_a":
-        sha = source_sha("gemm_fp8.hip", "device_common.hpp")
         if gemm_bound == "hbm":
             achieved, peak, unit, bound = kd["GB/s"], HBM_PEAK_GBS, "GB/s", "hbm"
         else:
             achieved, peak, unit, bound = kd["TFLOP/s"], FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
     else:
-        sha = source_sha("gemm_bf16.hip", "device_common.hpp")
         achieved, peak, unit, bound = kd["TFLOP/s"], BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     traffic = load_traffic(dominant, w.name, sha)
 

@@ -151,7 +151,9 @@ size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden);
  * wo_b != NULL, a4 over z.flatten(1) ([OPROJ] deep_gemm_fp8_o_proj).
  *  out  z bf16 [T][G][R] when wo_b == NULL, else y bf16 [T][hidden]
  *  wo_b bf16 [hidden][G*R] row-major or NULL (hidden ignored when NULL)
- * The activation scales follow scale_mode; the weight scales must match it. */
+ * The activation scales follow scale_mode; the weight scales must match it.
+ * Enqueues the quantisation kernel, the grouped GEMM and, with wo_b, the dense
+ * GEMM; every argument (wo_b included) is validated before the first launch. */
 oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const void* o,
                          const int64_t* positions, const float* cos_sin, const void* w_codes,
                          const float* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,

@@ -352,9 +352,104 @@ def test_fused_equals_steps(name):
     zs = torch.empty_like(zf)
     ap.oproj_grouped_wo_a(shp, 0, codes, scales, None, d_wq, d_ws, 0, zs)
     assert torch.equal(zf, zs)
+    # the workspace holds the same codes and scales (default layout, first two regions)
+    ncode = w.n_groups * w.T * w.D
+    assert torch.equal(ws[:ncode], codes.view(-1))
+    soff = (ncode + 255) // 256 * 256
+    assert torch.equal(ws[soff:soff + scales.numel() * 4].view(torch.int32), scales.view(-1).view(torch.int32))
     qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
     ref = oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank)
     assert U.rel_max_err(U.bf16_bits_to_f64(_host(zf).view(np.uint16)), ref) <= TOL
+
+
+@pytest.mark.parametrize("T,G,hpg,R,pow2,brows", [(32, 4, 8, 256, True, 1), (17, 3, 1, 128, False, 128),
+                                                  (9, 5, 2, 192, True, 128), (64, 2, 16, 64, False, 1)])
+def test_fused_small_batches(T, G, hpg, R, pow2, brows):
+    """oproj_fused on small batches equals the two separate calls bit for bit,
+    for every scale recipe and head-chunk size, and matches the oracle."""
+    w = wl.Workload(70 + T, f"f{T}", T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=R, max_pos=4096,
+                    positions="uniform", pow2=pow2, w_block_rows=brows)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    shp = _shape(w)
+    mode = int(pow2)
+    blk = ap.OPROJ_WBLOCK_1x128 if brows == 1 else ap.OPROJ_WBLOCK_128x128
+    d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    zf = torch.empty((T, G, R), dtype=torch.int16, device=DEV)
+    ap.oproj_fused(shp, mode, d_o, d_pos, d_tab, d_wq, d_ws, blk, None, 0, ws, nbytes, zf)
+    codes = torch.empty((G, T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((G, w.KB, T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, mode, d_o, d_pos, d_tab, codes, scales)
+    zs = torch.empty_like(zf)
+    ap.oproj_grouped_wo_a(shp, mode, codes, scales, None, d_wq, d_ws, blk, zs)
+    assert torch.equal(zf, zs)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, hpg, pow2=pow2)
+    ref = oracle.grouped_gemm(qr, sr, qwr, swr, G, R, brows)
+    assert U.rel_max_err(U.bf16_bits_to_f64(_host(zf).view(np.uint16)), ref) <= TOL
+
+
+def test_fused_decode_with_wo_b():
+    """The decode batch through oproj_fused with wo_b (a1..a4 in one call)."""
+    w = wl.WORKLOADS["decode"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    hidden = 512
+    wob = wl.bf16_matrix(wl.seed_of(94, 1), hidden, w.n_groups * w.o_lora_rank, 0.02)
+    shp = _shape(w)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, hidden)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    y = torch.empty((w.T, hidden), dtype=torch.int16, device=DEV)
+    ap.oproj_fused(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), d_wq, d_ws, 0,
+                   _dev(wob.view(np.int16)), hidden, ws, nbytes, y)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
+    zb = oracle.f64_to_bf16(oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank))
+    ref = oracle.dense_gemm_bf16(zb.reshape(w.T, -1), wob)
+    assert U.rel_max_err(U.bf16_bits_to_f64(_host(y).view(np.uint16)), ref) <= TOL
+
+
+def test_fused_decode_graph_replays():
+    """oproj_fused on the decode batch captured in a HIP graph: every replay
+    (with eager work and new inputs between replays) equals the eager result."""
+    w = wl.WORKLOADS["decode"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, _, _ = _weights_both(w)
+    shp = _shape(w)
+    d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    z = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+
+    def run():
+        ap.oproj_fused(shp, 0, d_o, d_pos, d_tab, d_wq, d_ws, 0, None, 0, ws, nbytes, z)
+
+    run()
+    ref0 = _host(z).copy()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    o2 = o.copy()
+    o2[::3] = o[::-1][::3]
+    for rep in range(4):
+        g.replay()
+        assert np.array_equal(_host(z), ref0), f"replay {rep}"
+        run()  # eager launch between replays
+        assert np.array_equal(_host(z), ref0)
+    d_o.copy_(_dev(o2.view(np.int16)))
+    run()
+    ref1 = _host(z).copy()
+    assert not np.array_equal(ref1, ref0)
+    for rep in range(2):
+        g.replay()
+        assert np.array_equal(_host(z), ref1), f"replay {rep} on new input"
 
 
 def test_full_path_with_wo_b_sampled():
