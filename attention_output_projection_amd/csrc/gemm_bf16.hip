@@ -6,17 +6,20 @@
 // wo_b(z.flatten(1))):
 //   y[m][j] = sum_c x[m][c] * w[j][c],  bf16 in, fp32 accumulate, bf16 out.
 //
-// Same pipeline as the FP8 tile kernel: 256x256 output tile per 512-thread
-// workgroup, eight waves as 2 (M) x 4 (N) of 128x64, one 64-deep K-step (128
-// bytes of every row) per stage, stages double-buffered in LDS (2 x 64 KiB)
-// and filled by DMA copies (global_load_lds) into XOR-swizzled 128-byte rows.
-// Waves 0-3 issue the copies, waves 4-7 only compute.  MFMA
-// v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a row (pieces 2q
-// and 2q+1 for lane group q) feed the two K=32 halves of the step, in the same
-// order for both operands, so the pair of MFMAs sums the whole 64-deep step.
-// The accumulators stay in the matrix-core result registers for the whole K
-// loop.  Tiles are walked in bands of four M-tiles (the N-tiles of a band share
-// its activation rows) and consecutive tiles are kept on one XCD.
+// Same pipeline as the FP8 tile kernel: 256 x (32*NI) output tile per
+// 512-thread workgroup, eight waves as 4 (M) x 2 (N) of 64 x (16*NI), one
+// 64-deep K-step (128 bytes of every row) per stage, stages double-buffered in
+// LDS and filled by DMA copies (global_load_lds) into XOR-swizzled 128-byte
+// rows.  Waves 0-3 issue the copies, waves 4-7 only compute.  NI = 8 gives
+// 256x256 tiles; NI = 7 gives 256x224 tiles, which the launcher picks when
+// they divide the grid into fuller rounds of 256 workgroups (hidden = 7168 =
+// 32 x 224).  MFMA v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a
+// row (pieces 2q and 2q+1 for lane group q) feed the two K=32 halves of the
+// step, in the same order for both operands, so the pair of MFMAs sums the
+// whole 64-deep step.  The accumulators stay in the matrix-core result
+// registers for the whole K loop.  Tiles are walked in bands of four M-tiles
+// (the N-tiles of a band share its activation rows) and consecutive tiles are
+// kept on one XCD.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -25,8 +28,7 @@ namespace oproj {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, NW = 8;
-constexpr int SA = 0, SB = BM * 128, STAGE = SB + BN * 128;  // 65536 bytes
+constexpr int BM = 256, NW = 8;
 constexpr int BAND = 4;  // M-tiles per band of the tile order
 
 struct DParams {
@@ -42,12 +44,15 @@ __device__ __forceinline__ int64_t xcd_remap_d(int64_t bid, int64_t nblocks) {
     return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
+template <int NI>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
+    constexpr int BN = 32 * NI;                          // tile columns
+    constexpr int SA = 0, SB = BM * 128, STAGE = SB + BN * 128;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[2][STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 3, wn = wave >> 2;
     const int64_t nblocks = p.mtiles * p.ntiles;
     const int64_t id = xcd_remap_d(blockIdx.x, nblocks);
     // band order: BAND M-tiles x all N-tiles, M fastest within the band
@@ -61,43 +66,46 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     const int64_t nstage = kbytes / 128;
 
     // ---- copy plan: copying wave c (0-3) moves activation rows 64c..64c+63
-    // and weight rows 64c..64c+63, 8 rows of 128 bytes per instruction;
-    // sources are uniform bases plus 32-bit lane offsets (the host keeps every
-    // offset below 2^32)
+    // and weight rows 8*NI*c..8*NI*c+8*NI-1, 8 rows of 128 bytes per
+    // instruction; sources are uniform bases plus 32-bit lane offsets (the
+    // host keeps every offset below 2^32)
     const bool copier = wave < 4;
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x);
     const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.w);
-    uint32_t off[16];
+    uint32_t aoff[8], woff[NI];
     if (copier) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int row = 64 * wave + 8 * j + (lane >> 3);
-            const int piece = (lane & 7) ^ swz(row);
             int64_t m = m0 + row;
             m = m < p.M ? m : p.M - 1;  // rows past M are computed but never stored
-            off[j] = (uint32_t)(m * kbytes + piece * 16);
+            aoff[j] = (uint32_t)(m * kbytes + ((lane & 7) ^ swz(row)) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int row = 8 * (NI * wave + j) + (lane >> 3);
             int64_t n = n0 + row;
             n = n < p.N ? n : p.N - 1;
-            off[8 + j] = (uint32_t)(n * kbytes + piece * 16);
+            woff[j] = (uint32_t)(n * kbytes + ((lane & 7) ^ swz(row)) * 16);
         }
     }
     const uint32_t ring0 = lds_offset(&ring[0][0]);
-    const uint32_t adst = ring0 + SA + 64 * (wave & 3) * 128, bdst = ring0 + SB + 64 * (wave & 3) * 128;
+    const uint32_t adst = ring0 + SA + 64 * (wave & 3) * 128, bdst = ring0 + SB + 8 * NI * (wave & 3) * 128;
     auto issue = [&](int64_t ks, int slot) __attribute__((always_inline)) {
         ks = ks < nstage ? ks : nstage - 1;  // past the end: re-copy the last step into a dead slot
         const uint32_t so = (uint32_t)(slot * STAGE);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dma16s(xb + ks * 128, off[j], adst + so + j * 1024);
+        for (int j = 0; j < 8; ++j) dma16s(xb + ks * 128, aoff[j], adst + so + j * 1024);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dma16s(wb + ks * 128, off[8 + j], bdst + so + j * 1024);
+        for (int j = 0; j < NI; ++j) dma16s(wb + ks * 128, woff[j], bdst + so + j * 1024);
     };
     if (copier) issue(0, 0);
 
-    v4f acc[8][4];
+    v4f acc[4][NI];
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // fragment addressing: rows 16k + frow share the swizzle of frow
     const int frow = lane & 15;
@@ -113,28 +121,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
         __builtin_amdgcn_s_barrier();  // ... and every other wave's; step ks-1 is free
         if (copier) issue(ks + 1, (int)((ks + 1) & 1));
         const uint8_t* st = ring[ks & 1];
-        const uint8_t* sta = st + SA + 128 * wm * 128;
-        const uint8_t* stb = st + SB + 64 * wn * 128;
-        v8bf blo[4], bhi[4];
+        const uint8_t* sta = st + SA + 64 * wm * 128;
+        const uint8_t* stb = st + SB + 16 * NI * wn * 128;
+        v8bf blo[NI], bhi[NI];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+        for (int ni = 0; ni < NI; ++ni) {
             blo[ni] = ld(stb + ni * 2048, lo_off);
             bhi[ni] = ld(stb + ni * 2048, hi_off);
         }
         // activation fragments of subtile mi+1 are read while subtile mi runs
         v8bf alo = ld(sta, lo_off), ahi = ld(sta, hi_off);
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
+        for (int mi = 0; mi < 4; ++mi) {
             const v8bf a0 = alo, a1 = ahi;
-            if (mi < 7) {
+            if (mi < 3) {
                 alo = ld(sta + (mi + 1) * 2048, lo_off);
                 ahi = ld(sta + (mi + 1) * 2048, hi_off);
             }
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, blo[ni], acc[mi][ni], 0, 0, 0);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bhi[ni], acc[mi][ni], 0, 0, 0);
         }
     }
@@ -142,13 +150,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
 
     // epilogue: bf16 (nearest even)
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
-                const int64_t col = n0 + 64 * wn + 16 * ni + frow;
+                const int64_t row = m0 + 64 * wm + 16 * mi + 4 * (lane >> 4) + i;
+                const int64_t col = n0 + 16 * NI * wn + 16 * ni + frow;
                 if (row < p.M && col < p.N) p.y[row * p.N + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
             }
 }
@@ -164,8 +172,16 @@ hipError_t launch_dense_bf16_gemm(const DenseGemmArgs& a, hipStream_t stream) {
     p.N = a.N;
     p.K = a.K;
     p.mtiles = (a.M + BM - 1) / BM;
-    p.ntiles = (a.N + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)(p.mtiles * p.ntiles)), dim3(NW * 64), 0, stream, p);
+    // 224-column tiles when they fill the last round of 256 workgroups better
+    const int64_t t256 = p.mtiles * ((a.N + 255) / 256), t224 = p.mtiles * ((a.N + 223) / 224);
+    auto fill = [](int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); };
+    const bool narrow = fill(t224) > fill(t256) + 0.02;
+    p.ntiles = narrow ? (a.N + 223) / 224 : (a.N + 255) / 256;
+    const dim3 grid((unsigned)(p.mtiles * p.ntiles)), block(NW * 64);
+    if (narrow)
+        hipLaunchKernelGGL(gemm_bf16_kernel<7>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(gemm_bf16_kernel<8>, grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

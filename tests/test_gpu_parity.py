@@ -322,9 +322,11 @@ def test_dense_bf16_gemm_parity():
     assert e <= TOL, e
 
 
-@pytest.mark.parametrize("M,N,K", [(600, 1040, 192), (1, 16, 64), (257, 272, 128), (513, 784, 320)])
+@pytest.mark.parametrize("M,N,K", [(600, 1040, 192), (1, 16, 64), (257, 272, 128), (513, 784, 320),
+                                   (2048, 1792, 128), (1800, 1776, 192)])
 def test_dense_bf16_gemm_ragged(M, N, K):
-    """Several 256x256 tiles with ragged M and N tails and odd step counts, checked densely."""
+    """Several tiles with ragged M and N tails and odd step counts, checked
+    densely; the last two shapes take the 256x224 tiles."""
     x = wl.bf16_matrix(wl.seed_of(92, M), M, K, 1.0)
     wb = wl.bf16_matrix(wl.seed_of(93, N), N, K, 0.02)
     y = torch.empty((M, N), dtype=torch.int16, device=DEV)
