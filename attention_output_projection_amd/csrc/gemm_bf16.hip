@@ -148,17 +148,38 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     }
     wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
 
-    // epilogue: bf16 (nearest even)
+    // epilogue: bf16 (nearest even) through LDS, so that y is written as whole
+    // tile rows with 16-byte stores; as many 64-row bands per pass as the ring
+    // holds (rows padded by 16 bytes against bank conflicts)
+    constexpr int EROW = BN + 8;                                   // bf16 per LDS row
+    constexpr int BANDS = (2 * STAGE) / (64 * EROW * 2) >= 4 ? 4 : 2;  // 64-row bands per pass
+    constexpr int CPR = BN / 8;                                    // 16-byte chunks per row
+    static_assert(64 * BANDS * EROW * 2 <= 2 * STAGE, "a pass of the epilogue fits in the ring");
+    uint16_t* stile = reinterpret_cast<uint16_t*>(&ring[0][0]);
+    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int pass = 0; pass < 4 / BANDS; ++pass) {
+        if (wm / BANDS == pass) {
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + 64 * wm + 16 * mi + 4 * (lane >> 4) + i;
-                const int64_t col = n0 + 16 * NI * wn + 16 * ni + frow;
-                if (row < p.M && col < p.N) p.y[row * p.N + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
-            }
+                for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 64 * (wm % BANDS) + 16 * mi + 4 * (lane >> 4) + i;
+                        const int c = 16 * NI * wn + 16 * ni + frow;
+                        stile[r * EROW + c] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
+                    }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 64 * BANDS * CPR; idx += NW * 64) {
+            const int r = idx / CPR, ch = idx % CPR;
+            const int64_t row = m0 + 64 * BANDS * pass + r, col = n0 + 8 * ch;
+            const uint4 v = *reinterpret_cast<const uint4*>(stile + r * EROW + 8 * ch);
+            if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(p.y + row * p.N + col) = v;
+        }
+        __syncthreads();
+    }
 }
 
 }  // namespace

@@ -96,6 +96,8 @@ __device__ __forceinline__ int64_t wscale_index(const GParams& p, int64_t wrow, 
 constexpr int TBM = 256, TBN = 256, TNS = 2, TNW = 8;
 constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
 constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
+constexpr int TEROW = TBN + 8;      // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
+static_assert(TBM * TEROW * 2 <= TNS * TSTAGE, "the epilogue tile fits in the ring");
 
 template <bool MX, bool W1>
 __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
@@ -241,18 +243,32 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     }
     wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
 
-    // epilogue: bf16 (nearest even), z[t][g][n]
+    // epilogue: bf16 (nearest even) through LDS, so that z[t][g][n] is written
+    // as whole 512-byte tile rows with 16-byte stores (a lane's results are
+    // one column of 4 rows, which would be 2-byte scattered stores)
+    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+    uint16_t* stile = reinterpret_cast<uint16_t*>(&ring[0][0]);  // [256][TEROW] bf16
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
-                const int64_t col = n0 + 64 * wn + 16 * ni + frow;
-                if (row < p.T && col < p.R)
-                    p.z[(row * p.G + g) * p.R + col] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
+                const int r = 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
+                const int c = 64 * wn + 16 * ni + frow;
+                stile[r * TEROW + c] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
             }
+    __syncthreads();
+    // 32 lanes per row, 16 bytes each; a wave stores 2 rows per instruction
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t col = n0 + 8 * l32;
+#pragma unroll 4
+    for (int k = 0; k < TBM / (2 * TNW); ++k) {
+        const int r = 2 * (TNW * k + wave) + half;
+        const int64_t row = m0 + r;
+        const uint4 v = *reinterpret_cast<const uint4*>(stile + r * TEROW + 8 * l32);
+        if (row < p.T && col < p.R) *reinterpret_cast<uint4*>(p.z + (row * p.G + g) * p.R + col) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -268,7 +284,13 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 // waves 2-3 only compute.  Rows are 128 bytes with the 16-byte pieces
 // XOR-swizzled, which makes the fragment reads conflict-free.  For the MFMAs the waves split N (wave w owns columns
 // 16w..16w+15); the K-groups' partial tiles are summed through LDS.
-constexpr int DBM = 64, DBN = 64, DNS = 4, DKS = 2;
+#ifndef OPROJ_DEC_DNS
+#define OPROJ_DEC_DNS 4
+#endif
+#ifndef OPROJ_DEC_DKS
+#define OPROJ_DEC_DKS 2
+#endif
+constexpr int DBM = 64, DBN = 64, DNS = OPROJ_DEC_DNS, DKS = OPROJ_DEC_DKS;
 constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
 constexpr int DVM = 9;  // copy instructions per copying wave per stage
 
