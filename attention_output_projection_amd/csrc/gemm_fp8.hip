@@ -293,6 +293,24 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 constexpr int DBM = 64, DBN = 64, DNS = OPROJ_DEC_DNS, DKS = OPROJ_DEC_DKS;
 constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
 constexpr int DVM = 9;  // copy instructions per copying wave per stage
+constexpr int DEROW = DBN + 8;  // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
+constexpr int DEPI = ((DKS - 1) * 256 * 16 * 4 + 1023) / 1024 * 1024;  // byte offset of the epilogue tile
+static_assert(DEPI + DBM * DEROW * 2 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
+
+// Wait until at most min(ahead, N) stages of this wave's copies are still in
+// flight (ahead < 0 counts as 0): the stage being waited for is followed by
+// `ahead` issued stages.
+template <int N>
+__device__ __forceinline__ void wait_stage(int64_t ahead) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= N)
+            wait_vmcnt<DVM * N>();
+        else
+            wait_stage<N - 1>(ahead);
+    }
+}
 
 // One workgroup's output tile (the whole decode pipeline); ring is the
 // workgroup's LDS.
@@ -311,7 +329,6 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // this K-group's K-blocks: [kb0, kb0 + nkb)
     const int64_t kb0 = p.KB * kq / DKS;
     const int64_t nkb = p.KB * (kq + 1) / DKS - kb0;
-    const int64_t klast = kb0 + (nkb > 0 ? nkb : 1) - 1;
 
     // ---- copy plan.  Copying wave c (0-1): activation rows 32c..32c+31 and
     // weight rows 32c..32c+31 (8 rows of 128 bytes per instruction), and one
@@ -350,8 +367,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     }
     const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
     auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
-        int64_t kb = kb0 + i;
-        kb = kb < klast ? kb : klast;  // tail stages re-copy the last block into a dead slot
+        const int64_t kb = kb0 + i;
         const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16s(abase + kb * 128, off[j], st + (32 * wave + 8 * j) * 128);
@@ -367,7 +383,8 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
 
     if (copier) {
 #pragma unroll
-        for (int s = 0; s < DNS - 1; ++s) issue(s, s);
+        for (int s = 0; s < DNS - 1; ++s)
+            if (s < nkb) issue(s, s);
     }
 
     v4f acc[4];
@@ -376,13 +393,14 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
 
     const int frow = lane & 15;
     const int p0 = 2 * (lane >> 4);
-    const int64_t nstages = p.KB / DKS + 1;  // >= nkb for every group: same barrier count
+    const int64_t nstages = (p.KB + DKS - 1) / DKS;  // the largest share: same barrier count in every group
     for (int64_t i = 0; i < nstages; ++i) {
-        // this wave's copies of stage i have landed (later stages' copies may
-        // still be in flight)
-        if (copier) wait_vmcnt<DVM * (DNS - 2)>();
+        // this wave's copies of stage i have landed; the copies of the stages
+        // after it that were issued (at most DNS-2, none past the group's
+        // last block) may still be in flight
+        if (copier) wait_stage<DNS - 2>(nkb - 1 - i);
         __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence)
-        if (copier) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
+        if (copier && i + DNS - 1 < nkb) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
         if (i >= nkb) continue;        // uniform per wave group
         const uint8_t* st = ring[kq][i % DNS];
         v8i bfr;
@@ -415,11 +433,14 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
             }
         }
     }
-    wait_vmcnt<0>();  // no copy may still be writing LDS
+    wait_vmcnt<0>();  // (already true: the last stage was waited for in full)
     __syncthreads();
 
-    // ---- sum the K groups through LDS (ring 0 of group 0 is free now)
-    float* red = reinterpret_cast<float*>(&ring[0][0][0]);
+    // ---- sum the K groups through LDS (the ring is free now); group 0 then
+    // stages the bf16 tile in LDS so that z is written as whole 128-byte tile
+    // rows with 16-byte stores
+    float* red = reinterpret_cast<float*>(&ring[0][0][0]);  // [DKS-1][256 lanes][16]
+    uint16_t* stile = reinterpret_cast<uint16_t*>(&ring[0][0][0] + DEPI);  // [64][DEROW]
     if constexpr (DKS > 1) {
         if (kq > 0) {
 #pragma unroll
@@ -428,24 +449,31 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
                 for (int i = 0; i < 4; ++i) red[((kq - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i] = acc[mi][i];
         }
         __syncthreads();
-        if (kq > 0) return;
+        if (kq == 0) {
 #pragma unroll
-        for (int q = 1; q < DKS; ++q)
+            for (int q = 1; q < DKS; ++q)
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mi][i] += red[((q - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i];
-    }
-
-    // ---- bf16 results of this wave's 16 columns
-    const int64_t col = n0 + 16 * wave + frow;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = m0 + mi * 16 + 4 * (lane >> 4) + i;
-            if (row < p.T && col < p.R) p.z[(row * p.G + g) * p.R + col] = (uint16_t)f32_to_bf16_bits(acc[mi][i]);
+                    for (int i = 0; i < 4; ++i)
+                        acc[mi][i] += red[((q - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i];
         }
+    }
+    if (kq == 0) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                stile[(16 * mi + 4 * (lane >> 4) + i) * DEROW + 16 * wave + frow] =
+                    (uint16_t)f32_to_bf16_bits(acc[mi][i]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < DBM * (DBN / 8); idx += DKS * 256) {
+        const int r = idx / (DBN / 8), ch = idx % (DBN / 8);
+        const int64_t row = m0 + r, col = n0 + 8 * ch;
+        const uint4 v = *reinterpret_cast<const uint4*>(stile + r * DEROW + 8 * ch);
+        if (row < p.T && col < p.R) *reinterpret_cast<uint4*>(p.z + (row * p.G + g) * p.R + col) = v;
+    }
 }
 
 template <bool MX, bool W1>
