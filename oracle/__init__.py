@@ -61,8 +61,10 @@ def _load():
         lib.orc_grouped_gemm.argtypes = [I64, I64, I64, I64, P, P, I64, I64, I64, I64, I64, P, P,
                                          I64, P, I64, P, INT]
         lib.orc_dense_gemm_bf16.argtypes = [I64, I64, I64, P, P, P, I64, P, INT]
+        lib.orc_inv_rope_bf16.argtypes = [I64, I64, I64, I64, P, P, P, P]
         for f in (lib.orc_rope_f32, lib.orc_block_quant_rows, lib.orc_inv_rope_quant,
-                  lib.orc_quant_weight, lib.orc_grouped_gemm, lib.orc_dense_gemm_bf16):
+                  lib.orc_quant_weight, lib.orc_grouped_gemm, lib.orc_dense_gemm_bf16,
+                  lib.orc_inv_rope_bf16):
             f.restype = None
         _lib = lib
     return _lib
@@ -124,6 +126,20 @@ def rope_f32(x, positions, table, nope_dim: int, rope_dim: int, inverse: bool = 
     T, H, hd = x.shape
     assert hd == nope_dim + rope_dim and tab.shape[1] == rope_dim
     _load().orc_rope_f32(T, H, nope_dim, rope_dim, _p(x), _p(pos), _p(tab), -1 if inverse else 1)
+    return x
+
+
+def inv_rope_bf16(o_bf16, positions, table, nope_dim: int = 448, rope_dim: int = 64) -> np.ndarray:
+    """Unquantised a1: bf16 bits o[T, H, head_dim] -> bf16 bits x[T, H, head_dim]
+    (rotated dims rounded to bf16, the rest copied); view it as [T, G, D]."""
+    o = _c(o_bf16, np.uint16)
+    pos = _c(positions, np.int64)
+    tab = _c(table, np.float32)
+    T, H, hd = o.shape
+    assert hd == nope_dim + rope_dim and tab.shape[1] == rope_dim
+    assert np.all((pos >= 0) & (pos < tab.shape[0]))
+    x = np.empty_like(o)
+    _load().orc_inv_rope_bf16(T, H, nope_dim, rope_dim, _p(o), _p(pos), _p(tab), _p(x))
     return x
 
 
@@ -224,3 +240,32 @@ def dense_gemm_bf16(x_bf16, w_bf16, idx=None, nthreads: int | None = None) -> np
     y = np.empty(idx.shape[0], np.float64)
     lib.orc_dense_gemm_bf16(M, N, K, _p(x), _p(w), _p(idx), idx.shape[0], _p(y), nt)
     return y
+
+
+# ---------------------------------------------------------------- a3 unquantised
+def grouped_gemm_bf16(x_bf16, w_bf16, n_groups: int, o_lora_rank: int, idx=None,
+                      nthreads: int | None = None) -> np.ndarray:
+    """fp64 grouped contraction of bf16 operands: one matmul per group,
+    z[t, g, n] = sum_k x[t, g, k] * w[g*R + n, k].
+
+    ``x_bf16`` is [T, G, D] (any strides numpy can view), ``w_bf16`` [G*R, D].
+    Dense result [T, G, R], or the values at int64 (t, g, n) triples ``idx``."""
+    x = np.asarray(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    T, G, D = x.shape
+    R = o_lora_rank
+    assert G == n_groups and w.shape == (G * R, D)
+    if idx is None:
+        z = np.empty((T, G, R), np.float64)
+        for g in range(G):
+            z[:, g, :] = dense_gemm_bf16(np.ascontiguousarray(x[:, g, :]), w[g * R:(g + 1) * R],
+                                         nthreads=nthreads)
+        return z
+    idx = _c(idx, np.int64).reshape(-1, 3)
+    z = np.empty(idx.shape[0], np.float64)
+    for g in np.unique(idx[:, 1]):
+        sel = np.nonzero(idx[:, 1] == g)[0]
+        pairs = np.stack([idx[sel, 0], idx[sel, 2]], axis=1)
+        z[sel] = dense_gemm_bf16(np.ascontiguousarray(x[:, g, :]), w[g * R:(g + 1) * R], idx=pairs,
+                                 nthreads=nthreads)
+    return z

@@ -38,6 +38,11 @@
  *      over 128x128 tiles of the flat [G*R, D] matrix or 1x128 per-row blocks.
  *  R8  grouped GEMM accumulates in fp64; z rounds once fp64 -> bf16 (nearest
  *      even) when it feeds wo_b; wo_b accumulates in fp64.
+ *  R9  unquantised path ([GWA] grouped_input calls the fused kernel with
+ *      quantize=False and returns bf16 groups): the rotated dims are rounded
+ *      fp32 -> bf16 to nearest even; dims 0..nope-1 are copied unchanged.  The
+ *      grouped bf16 contraction ([OPROJ] deep_gemm_fp8_o_proj without FP8:
+ *      one matmul per group) accumulates in fp64.
  */
 #include <math.h>
 #include <pthread.h>
@@ -289,6 +294,28 @@ void orc_inv_rope_quant(int64_t T, int64_t G, int64_t hpg, int64_t nope, int64_t
         pthread_create(&th[i], NULL, orc_irq_worker, &jobs[i]);
     }
     for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
+/* Unquantised step a1 (R1, R2, R9): o[T][H][head_dim] bf16 -> x bf16 in the
+ * same token-major layout, i.e. [T][G][hpg*head_dim] ([GWA] grouped_input's
+ * [num_tokens, n_groups, group_dim] view of the heads). */
+void orc_inv_rope_bf16(int64_t T, int64_t H, int64_t nope, int64_t rope, const uint16_t* o,
+                       const int64_t* pos, const float* table, uint16_t* x) {
+    int64_t hd = nope + rope;
+    float* row = (float*)malloc((size_t)hd * sizeof(float));
+    for (int64_t t = 0; t < T; ++t) {
+        const float* trow = table + pos[t] * rope;
+        for (int64_t h = 0; h < H; ++h) {
+            const uint16_t* src = o + (t * H + h) * hd;
+            uint16_t* dst = x + (t * H + h) * hd;
+            for (int64_t k = 0; k < hd; ++k) row[k] = orc_bf16_to_f32(src[k]);
+            orc_inv_rope_row(row, nope, rope, trow);
+            for (int64_t k = 0; k < nope; ++k) dst[k] = src[k];
+            /* fp32 -> fp64 is exact, so this is the nearest-even bf16 of the fp32 value */
+            for (int64_t k = nope; k < hd; ++k) dst[k] = orc_f64_to_bf16((double)row[k]);
+        }
+    }
+    free(row);
 }
 
 /* ------------------------------------------------------------------ */

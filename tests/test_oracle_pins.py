@@ -525,6 +525,91 @@ def test_dense_bf16_gemm_matches_numpy():
     assert np.array_equal(oracle.dense_gemm_bf16(x, w, idx=idx), y[idx[:, 0], idx[:, 1]])
 
 
+# ---------------------------------------------------------------- unquantised path
+def _bf16_rows(T, H, seed):
+    return wl.normal_bf16(seed, T * H * 512).reshape(T, H, 512)
+
+
+def test_inv_rope_bf16_position0_and_nope_passthrough():
+    o = _bf16_rows(3, 4, 31)
+    tab = wl.cos_sin_table(4096, 64)
+    x0 = oracle.inv_rope_bf16(o, np.zeros(3, np.int64), tab)
+    assert np.array_equal(x0, o)  # cos 0 = 1, sin 0 = 0: the identity, bit for bit
+    x = oracle.inv_rope_bf16(o, np.array([7, 1000, 4095], np.int64), tab)
+    assert np.array_equal(x[..., :448], o[..., :448])
+    assert (x[..., 448:] != o[..., 448:]).mean() > 0.5
+
+
+def test_inv_rope_bf16_is_the_fp32_rotation_rounded_by_torch():
+    """Library route for the rounding: torch's fp32 -> bfloat16 conversion
+    (nearest even) of the pinned fp32 rotation."""
+    o = _bf16_rows(5, 3, 32)
+    tab = wl.cos_sin_table(32768, 64)
+    pos = np.array([1, 77, 4000, 20000, 32767], np.int64)
+    x = oracle.inv_rope_bf16(o, pos, tab)
+    r32 = oracle.rope_f32(wl.bf16_bits_to_f32(o), pos, tab, 448, 64, inverse=True)
+    want = torch.from_numpy(np.ascontiguousarray(r32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(x.view(np.int16), want)
+
+
+def test_inv_rope_bf16_error_bound_against_exact_rotation():
+    """fp64 complex closed form; bf16 keeps 8 significant bits, so the result
+    is within half a bf16 ulp of the exact value plus the fp32 rounding."""
+    o = _bf16_rows(6, 2, 33)
+    tab = wl.cos_sin_table(8192, 64)
+    pos = np.array([0, 3, 33, 333, 3333, 8191], np.int64)
+    x = wl.bf16_bits_to_f32(oracle.inv_rope_bf16(o, pos, tab)).astype(np.float64)
+    of = wl.bf16_bits_to_f32(o).astype(np.float64)
+    z = of[..., 448::2] + 1j * of[..., 449::2]
+    cs = tab[pos, :32].astype(np.float64) + 1j * tab[pos, 32:].astype(np.float64)
+    want = z * np.conj(cs)[:, None, :]
+    for got, ref in ((x[..., 448::2], want.real), (x[..., 449::2], want.imag)):
+        bound = np.abs(ref) * 2.0 ** -8 + np.abs(z) * 2.0 ** -21 + 1e-30
+        assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_grouped_gemm_bf16_bruteforce_tiny():
+    """Pure-Python fp64 loops over the definition, one matmul per group."""
+    T, G, D, R = 3, 2, 16, 5
+    x = wl.normal_bf16(34, T * G * D).reshape(T, G, D)
+    w = wl.normal_bf16(35, G * R * D, std=0.02).reshape(G * R, D)
+    xf, wf = wl.bf16_bits_to_f32(x), wl.bf16_bits_to_f32(w)
+    z = oracle.grouped_gemm_bf16(x, w, G, R)
+    for t in range(T):
+        for g in range(G):
+            for n in range(R):
+                acc = 0.0
+                for k in range(D):
+                    acc += float(xf[t, g, k]) * float(wf[g * R + n, k])
+                assert abs(z[t, g, n] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_grouped_gemm_bf16_integer_operands_exact():
+    """Small integers are exact in bf16 and in fp64 sums: closed form."""
+    T, G, D, R = 4, 3, 64, 8
+    rng = np.random.default_rng(36)
+    xi = rng.integers(-8, 9, (T, G, D))
+    wi = rng.integers(-8, 9, (G * R, D))
+    x = wl.f32_to_bf16_bits(xi.astype(np.float32))
+    w = wl.f32_to_bf16_bits(wi.astype(np.float32))
+    z = oracle.grouped_gemm_bf16(x, w, G, R)
+    want = np.einsum("tgk,gnk->tgn", xi, wi.reshape(G, R, D))
+    assert np.array_equal(z, want.astype(np.float64))
+
+
+def test_grouped_gemm_bf16_group_isolation_and_samples():
+    T, G, D, R = 4, 3, 32, 6
+    x = wl.normal_bf16(37, T * G * D).reshape(T, G, D)
+    w = wl.normal_bf16(38, G * R * D, std=0.02).reshape(G * R, D)
+    z = oracle.grouped_gemm_bf16(x, w, G, R)
+    w2 = w.copy()
+    w2[R:2 * R] = wl.f32_to_bf16_bits(np.full((R, D), 3.0, np.float32))  # rows of group 1 only
+    z2 = oracle.grouped_gemm_bf16(x, w2, G, R)
+    assert np.array_equal(z2[:, [0, 2]], z[:, [0, 2]]) and not np.array_equal(z2[:, 1], z[:, 1])
+    idx = np.array([[0, 0, 0], [3, 2, 5], [1, 1, 3]], np.int64)
+    assert np.array_equal(oracle.grouped_gemm_bf16(x, w, G, R, idx=idx), z[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
 # ---------------------------------------------------------------- generator pins
 def test_splitmix64_reference_outputs():
     """First outputs of SplitMix64 seeded with 0 (Vigna's reference generator)."""
