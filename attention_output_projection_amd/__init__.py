@@ -1,5 +1,6 @@
 """MI355X (gfx950) O-projection front half: inverse RoPE -> 1x128 FP8 e4m3fn
-quantisation -> grouped wo_a GEMM [-> dense wo_b GEMM].
+quantisation -> grouped wo_a GEMM [-> dense wo_b GEMM], plus the unquantised
+variant (bf16 inverse RoPE -> grouped bf16 wo_a GEMM).
 
 The compute runs in the HIP library ``liboproj.so`` (C ABI in
 ``include/oproj.h``).  This package is the thin Python binding over it:
@@ -14,6 +15,7 @@ from ._native import (  # noqa: F401
     OPROJ_WBLOCK_1x128,
     OPROJ_WBLOCK_128x128,
     ActLayout,
+    Bf16Layout,
     OprojError,
     Shape,
     default_layout,
@@ -23,6 +25,8 @@ from ._native import (  # noqa: F401
     oproj_fused,
     oproj_fused_workspace_bytes,
     oproj_grouped_wo_a,
+    oproj_grouped_wo_a_bf16,
+    oproj_inv_rope_bf16,
     oproj_inv_rope_quant,
     oproj_quantize_weight,
     oproj_status_string,

@@ -35,6 +35,10 @@ class _Layout(ctypes.Structure):
                                               "s_stride_kb")]
 
 
+class _Bf16Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("stride_t", "stride_g")]
+
+
 @dataclasses.dataclass
 class Shape:
     T: int
@@ -73,6 +77,17 @@ class ActLayout:
         return _Layout(self.stride_t, self.stride_g, self.s_stride_t, self.s_stride_g, self.s_stride_kb)
 
 
+@dataclasses.dataclass
+class Bf16Layout:
+    """Element strides of a bf16 activation operand x(t, g, k)."""
+
+    stride_t: int
+    stride_g: int
+
+    def _c(self) -> _Bf16Layout:
+        return _Bf16Layout(self.stride_t, self.stride_g)
+
+
 def default_layout(shape: Shape) -> ActLayout:
     """Group-major codes [G][T][D] and MN-major scales [G][KB][T]."""
     return ActLayout(shape.D, shape.T * shape.D, 1, shape.KB * shape.T, shape.T)
@@ -94,10 +109,12 @@ def load_library():
                                "`python -m attention_output_projection_amd.build`")
         lib = ctypes.CDLL(_LIB_PATH)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        SP, LP = ctypes.POINTER(_Shape), ctypes.POINTER(_Layout)
+        SP, LP, BP = ctypes.POINTER(_Shape), ctypes.POINTER(_Layout), ctypes.POINTER(_Bf16Layout)
         sig = {
             "oproj_inv_rope_quant": (I32, [SP, I32, P, P, P, P, P, LP, P]),
             "oproj_grouped_wo_a": (I32, [SP, I32, P, P, LP, P, P, I32, P, P]),
+            "oproj_inv_rope_bf16": (I32, [SP, P, P, P, P, BP, P]),
+            "oproj_grouped_wo_a_bf16": (I32, [SP, P, BP, P, P, P]),
             "oproj_dense_bf16_gemm": (I32, [I64, I64, I64, P, P, P, P]),
             "oproj_fused_workspace_bytes": (SZ, [SP, I64]),
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
@@ -165,6 +182,20 @@ def oproj_grouped_wo_a(shape: Shape, scale_mode: int, a_codes, a_scales, a_layou
         ctypes.byref(shape._c()), scale_mode, _ptr(a_codes), _ptr(a_scales), _lay(a_layout),
         _ptr(w_codes), _ptr(w_scales), w_block, _ptr(z), _stream(stream))
     _check("oproj_grouped_wo_a", st)
+
+
+def oproj_inv_rope_bf16(shape: Shape, o, positions, cos_sin, x, x_layout: Bf16Layout | None = None,
+                        stream=None) -> None:
+    st = load_library().oproj_inv_rope_bf16(
+        ctypes.byref(shape._c()), _ptr(o), _ptr(positions), _ptr(cos_sin), _ptr(x), _lay(x_layout),
+        _stream(stream))
+    _check("oproj_inv_rope_bf16", st)
+
+
+def oproj_grouped_wo_a_bf16(shape: Shape, x, x_layout: Bf16Layout | None, w, z, stream=None) -> None:
+    st = load_library().oproj_grouped_wo_a_bf16(
+        ctypes.byref(shape._c()), _ptr(x), _lay(x_layout), _ptr(w), _ptr(z), _stream(stream))
+    _check("oproj_grouped_wo_a_bf16", st)
 
 
 def oproj_dense_bf16_gemm(M: int, N: int, K: int, x, w, y, stream=None) -> None:

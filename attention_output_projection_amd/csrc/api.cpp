@@ -195,6 +195,80 @@ oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* 
     return from_hip(oproj::launch_dense_bf16_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// default and validated layout of a bf16 activation operand
+oproj_status bf16_layout(const oproj_shape* s, const oproj_bf16_layout* l, int64_t* st, int64_t* sg) {
+    const int64_t D = s->heads_per_group * 512;
+    if (!l) {
+        *st = s->n_groups * D;
+        *sg = D;
+        return OPROJ_OK;
+    }
+    if (l->stride_t < 0 || l->stride_g < 0) return OPROJ_E_SHAPE;
+    if (l->stride_t % 8 != 0 || l->stride_g % 8 != 0) return OPROJ_E_ALIGN;
+    *st = l->stride_t;
+    *sg = l->stride_g;
+    return OPROJ_OK;
+}
+
+}  // namespace
+
+oproj_status oproj_inv_rope_bf16(const oproj_shape* shape, const void* o, const int64_t* positions,
+                                 const float* cos_sin, void* x, const oproj_bf16_layout* x_layout,
+                                 void* stream) {
+    oproj_status st = check_shape(shape, false);
+    if (st != OPROJ_OK) return st;
+    int64_t xst, xsg;
+    if ((st = bf16_layout(shape, x_layout, &xst, &xsg)) != OPROJ_OK) return st;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!o || !positions || !cos_sin || !x) return OPROJ_E_NULL;
+    if (!aligned16(o) || !aligned16(cos_sin) || !aligned16(x) || (reinterpret_cast<uintptr_t>(positions) & 7u))
+        return OPROJ_E_ALIGN;
+    oproj::RopeBf16Args a;
+    a.T = shape->T;
+    a.G = shape->n_groups;
+    a.hpg = shape->heads_per_group;
+    a.max_pos = shape->max_pos;
+    a.o = static_cast<const uint16_t*>(o);
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.x = static_cast<uint16_t*>(x);
+    a.stride_t = xst;
+    a.stride_g = xsg;
+    return from_hip(oproj::launch_inv_rope_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+oproj_status oproj_grouped_wo_a_bf16(const oproj_shape* shape, const void* x,
+                                     const oproj_bf16_layout* x_layout, const void* w, void* z,
+                                     void* stream) {
+    oproj_status st = check_shape(shape, true);
+    if (st != OPROJ_OK) return st;
+    int64_t xst, xsg;
+    if ((st = bf16_layout(shape, x_layout, &xst, &xsg)) != OPROJ_OK) return st;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!x || !w || !z) return OPROJ_E_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(z)) return OPROJ_E_ALIGN;
+    const int64_t D = shape->heads_per_group * 512, R = shape->o_lora_rank, G = shape->n_groups;
+    // the kernel addresses a group's operands as a uniform base plus 32-bit lane offsets
+    const int64_t lim = int64_t(1) << 32;
+    if ((shape->T - 1) * xst * 2 + D * 2 > lim || R * D * 2 > lim) return OPROJ_E_SHAPE;
+    oproj::Bf16GemmArgs a;
+    a.G = G;
+    a.M = shape->T;
+    a.N = R;
+    a.K = D;
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w);
+    a.y = static_cast<uint16_t*>(z);
+    a.sx = xst;
+    a.gx = xsg;
+    a.gw = R * D;
+    a.sy = G * R;
+    a.gy = R;
+    return from_hip(oproj::launch_bf16_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden) {
     if (check_shape(shape, true) != OPROJ_OK) return 0;
     const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;

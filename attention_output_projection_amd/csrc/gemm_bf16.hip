@@ -1,10 +1,13 @@
-// gemm_bf16.hip -- step a4 on gfx950: the dense wo_b GEMM over the flattened
-// z (sglang source page "python/sglang/srt/models/deepseek_v4.py",
-// MQALayer.forward: wo_b is applied to z.flatten(1); wo_b is a linear layer
-// from G*R to hidden, weight [hidden, G*R]; vLLM API page
-// "vllm.models.deepseek_v4.nvidia.ops.o_proj", deep_gemm_fp8_o_proj ends with
-// wo_b(z.flatten(1))):
-//   y[m][j] = sum_c x[m][c] * w[j][c],  bf16 in, fp32 accumulate, bf16 out.
+// gemm_bf16.hip -- bf16 GEMMs on gfx950, y[m][j] = sum_c x[m][c] * w[j][c]
+// with bf16 inputs, fp32 accumulation and bf16 output, for
+//  * step a4, the dense wo_b GEMM over the flattened z (sglang source page
+//    "python/sglang/srt/models/deepseek_v4.py", MQALayer.forward: wo_b is
+//    applied to z.flatten(1), a linear layer from G*R to hidden with weight
+//    [hidden, G*R]; vLLM API page "vllm.models.deepseek_v4.nvidia.ops.o_proj",
+//    deep_gemm_fp8_o_proj ends with wo_b(z.flatten(1)));
+//  * the unquantised grouped wo_a (same page, deep_gemm_fp8_o_proj without
+//    FP8: a batched matmul of the bf16 groups [G, T, D] with wo_a viewed
+//    [G, R, D]), one independent GEMM per group with strided operands.
 //
 // Same pipeline as the FP8 tile kernel: 256 x (32*NI) output tile per
 // 512-thread workgroup, eight waves as 4 (M) x 2 (N) of 64 x (16*NI), one
@@ -13,7 +16,8 @@
 // rows.  Waves 0-3 issue the copies, waves 4-7 only compute.  NI = 8 gives
 // 256x256 tiles; NI = 7 gives 256x224 tiles, which the launcher picks when
 // they divide the grid into fuller rounds of 256 workgroups (hidden = 7168 =
-// 32 x 224).  MFMA v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a
+// 32 x 224); NI = 2 gives 256x64 tiles for grids too small to fill the
+// chip with wide tiles (few tokens).  MFMA v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a
 // row (pieces 2q and 2q+1 for lane group q) feed the two K=32 halves of the
 // step, in the same order for both operands, so the pair of MFMAs sums the
 // whole 64-deep step.  The accumulators stay in the matrix-core result
@@ -36,7 +40,8 @@ struct DParams {
     const uint16_t* w;
     uint16_t* y;
     int64_t M, N, K;
-    int64_t mtiles, ntiles;
+    int64_t sx, sy, gx, gw, gy;  // row and group strides, elements
+    int64_t G, mtiles, ntiles;   // tiles per group: mtiles x ntiles
 };
 
 __device__ __forceinline__ int64_t xcd_remap_d(int64_t bid, int64_t nblocks) {
@@ -53,8 +58,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int wm = wave & 3, wn = wave >> 2;
-    const int64_t nblocks = p.mtiles * p.ntiles;
-    const int64_t id = xcd_remap_d(blockIdx.x, nblocks);
+    const int64_t per = p.mtiles * p.ntiles;
+    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per);
+    const int64_t g = gid / per, id = gid - g * per;
     // band order: BAND M-tiles x all N-tiles, M fastest within the band
     const int64_t band = id / (BAND * p.ntiles);
     const int64_t mfirst = band * BAND;
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     const int64_t local = id - band * BAND * p.ntiles;
     const int64_t mt = mfirst + local % bh, nt = local / bh;
     const int64_t m0 = mt * BM, n0 = nt * BN;
-    const int64_t kbytes = p.K * 2;
+    const int64_t kbytes = p.K * 2, xrow = p.sx * 2;
     const int64_t nstage = kbytes / 128;
 
     // ---- copy plan: copying wave c (0-3) moves activation rows 64c..64c+63
@@ -70,8 +76,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     // instruction; sources are uniform bases plus 32-bit lane offsets (the
     // host keeps every offset below 2^32)
     const bool copier = wave < 4;
-    const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x);
-    const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.w);
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x + g * p.gx);
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.w + g * p.gw);
     uint32_t aoff[8], woff[NI];
     if (copier) {
 #pragma unroll
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
             const int row = 64 * wave + 8 * j + (lane >> 3);
             int64_t m = m0 + row;
             m = m < p.M ? m : p.M - 1;  // rows past M are computed but never stored
-            aoff[j] = (uint32_t)(m * kbytes + ((lane & 7) ^ swz(row)) * 16);
+            aoff[j] = (uint32_t)(m * xrow + ((lane & 7) ^ swz(row)) * 16);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
             const int r = idx / CPR, ch = idx % CPR;
             const int64_t row = m0 + 64 * BANDS * pass + r, col = n0 + 8 * ch;
             const uint4 v = *reinterpret_cast<const uint4*>(stile + r * EROW + 8 * ch);
-            if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(p.y + row * p.N + col) = v;
+            if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(p.y + g * p.gy + row * p.sy + col) = v;
         }
         __syncthreads();
     }
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
 
 }  // namespace
 
-hipError_t launch_dense_bf16_gemm(const DenseGemmArgs& a, hipStream_t stream) {
+hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
     DParams p;
     p.x = a.x;
     p.w = a.w;
@@ -192,18 +198,47 @@ hipError_t launch_dense_bf16_gemm(const DenseGemmArgs& a, hipStream_t stream) {
     p.M = a.M;
     p.N = a.N;
     p.K = a.K;
+    p.sx = a.sx;
+    p.sy = a.sy;
+    p.gx = a.gx;
+    p.gw = a.gw;
+    p.gy = a.gy;
+    p.G = a.G;
     p.mtiles = (a.M + BM - 1) / BM;
-    // 224-column tiles when they fill the last round of 256 workgroups better
-    const int64_t t256 = p.mtiles * ((a.N + 255) / 256), t224 = p.mtiles * ((a.N + 223) / 224);
+    // 64-column tiles when 256-column tiles leave most of the chip idle;
+    // otherwise 224-column tiles when they fill the last round of 256
+    // workgroups better than 256-column tiles
+    const int64_t t256 = a.G * p.mtiles * ((a.N + 255) / 256), t224 = a.G * p.mtiles * ((a.N + 223) / 224);
     auto fill = [](int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); };
-    const bool narrow = fill(t224) > fill(t256) + 0.02;
-    p.ntiles = narrow ? (a.N + 223) / 224 : (a.N + 255) / 256;
-    const dim3 grid((unsigned)(p.mtiles * p.ntiles)), block(NW * 64);
-    if (narrow)
+    int ni = 8;
+    if (t256 < 128)
+        ni = 2;
+    else if (fill(t224) > fill(t256) + 0.02)
+        ni = 7;
+    p.ntiles = (a.N + 32 * ni - 1) / (32 * ni);
+    const dim3 grid((unsigned)(a.G * p.mtiles * p.ntiles)), block(NW * 64);
+    if (ni == 2)
+        hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, block, 0, stream, p);
+    else if (ni == 7)
         hipLaunchKernelGGL(gemm_bf16_kernel<7>, grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL(gemm_bf16_kernel<8>, grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+hipError_t launch_dense_bf16_gemm(const DenseGemmArgs& a, hipStream_t stream) {
+    Bf16GemmArgs b;
+    b.G = 1;
+    b.M = a.M;
+    b.N = a.N;
+    b.K = a.K;
+    b.x = a.x;
+    b.w = a.w;
+    b.y = a.y;
+    b.sx = a.K;
+    b.sy = a.N;
+    b.gx = b.gw = b.gy = 0;
+    return launch_bf16_gemm(b, stream);
 }
 
 }  // namespace oproj

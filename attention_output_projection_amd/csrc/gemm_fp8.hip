@@ -283,7 +283,8 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 // copies (a copy waits at issue while the CU's memory pipeline is full) and
 // waves 2-3 only compute.  Rows are 128 bytes with the 16-byte pieces
 // XOR-swizzled, which makes the fragment reads conflict-free.  For the MFMAs the waves split N (wave w owns columns
-// 16w..16w+15); the K-groups' partial tiles are summed through LDS.
+// 16w..16w+15); the K-groups' partial tiles are summed through LDS and
+// written as whole 128-byte rows of z.
 #ifndef OPROJ_DEC_DNS
 #define OPROJ_DEC_DNS 4
 #endif
@@ -293,9 +294,8 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 constexpr int DBM = 64, DBN = 64, DNS = OPROJ_DEC_DNS, DKS = OPROJ_DEC_DKS;
 constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
 constexpr int DVM = 9;  // copy instructions per copying wave per stage
-constexpr int DEROW = DBN + 8;  // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
-constexpr int DEPI = ((DKS - 1) * 256 * 16 * 4 + 1023) / 1024 * 1024;  // byte offset of the epilogue tile
-static_assert(DEPI + DBM * DEROW * 2 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
+constexpr int DPROW = DBN + 4;  // fp32 per row of an epilogue partial tile (pad against bank conflicts)
+static_assert(DKS * DBM * DPROW * 4 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
 
 // Wait until at most min(ahead, N) stages of this wave's copies are still in
 // flight (ahead < 0 counts as 0): the stage being waited for is followed by
@@ -436,42 +436,32 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     wait_vmcnt<0>();  // (already true: the last stage was waited for in full)
     __syncthreads();
 
-    // ---- sum the K groups through LDS (the ring is free now); group 0 then
-    // stages the bf16 tile in LDS so that z is written as whole 128-byte tile
-    // rows with 16-byte stores
-    float* red = reinterpret_cast<float*>(&ring[0][0][0]);  // [DKS-1][256 lanes][16]
-    uint16_t* stile = reinterpret_cast<uint16_t*>(&ring[0][0][0] + DEPI);  // [64][DEROW]
-    if constexpr (DKS > 1) {
-        if (kq > 0) {
+    // ---- each K-group's fp32 partial tile into LDS (the ring is free now),
+    // then every thread sums one 8-column chunk of one row over the K-groups
+    // and writes it to z as bf16: whole 128-byte tile rows, 16-byte stores
+    float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [DKS][64][DPROW]
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) red[((kq - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i] = acc[mi][i];
-        }
-        __syncthreads();
-        if (kq == 0) {
-#pragma unroll
-            for (int q = 1; q < DKS; ++q)
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[mi][i] += red[((q - 1) * 256 + (wave * 64 + lane)) * 16 + mi * 4 + i];
-        }
-    }
-    if (kq == 0) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                stile[(16 * mi + 4 * (lane >> 4) + i) * DEROW + 16 * wave + frow] =
-                    (uint16_t)f32_to_bf16_bits(acc[mi][i]);
-    }
+        for (int i = 0; i < 4; ++i)
+            part[(kq * DBM + 16 * mi + 4 * (lane >> 4) + i) * DPROW + 16 * wave + frow] = acc[mi][i];
     __syncthreads();
     for (int idx = tid; idx < DBM * (DBN / 8); idx += DKS * 256) {
         const int r = idx / (DBN / 8), ch = idx % (DBN / 8);
+        float4 s0 = *reinterpret_cast<const float4*>(part + r * DPROW + 8 * ch);
+        float4 s1 = *reinterpret_cast<const float4*>(part + r * DPROW + 8 * ch + 4);
+#pragma unroll
+        for (int q = 1; q < DKS; ++q) {
+            const float4 u0 = *reinterpret_cast<const float4*>(part + (q * DBM + r) * DPROW + 8 * ch);
+            const float4 u1 = *reinterpret_cast<const float4*>(part + (q * DBM + r) * DPROW + 8 * ch + 4);
+            s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
+            s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+        }
+        const uint4 v = {f32_to_bf16_bits(s0.x) | (f32_to_bf16_bits(s0.y) << 16),
+                         f32_to_bf16_bits(s0.z) | (f32_to_bf16_bits(s0.w) << 16),
+                         f32_to_bf16_bits(s1.x) | (f32_to_bf16_bits(s1.y) << 16),
+                         f32_to_bf16_bits(s1.z) | (f32_to_bf16_bits(s1.w) << 16)};
         const int64_t row = m0 + r, col = n0 + 8 * ch;
-        const uint4 v = *reinterpret_cast<const uint4*>(stile + r * DEROW + 8 * ch);
         if (row < p.T && col < p.R) *reinterpret_cast<uint4*>(p.z + (row * p.G + g) * p.R + col) = v;
     }
 }

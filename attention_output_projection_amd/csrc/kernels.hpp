@@ -46,6 +46,28 @@ struct GroupedGemmArgs {
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t s);
 
+struct RopeBf16Args {
+    int64_t T, G, hpg, max_pos;
+    const uint16_t* o;         // bf16 [T][G*hpg][512]
+    const int64_t* positions;  // [T]
+    const float* cos_sin;      // [max_pos][64]
+    uint16_t* x;               // bf16 x(t, g, k) at x[t*stride_t + g*stride_g + k]
+    int64_t stride_t, stride_g;
+};
+hipError_t launch_inv_rope_bf16(const RopeBf16Args& a, hipStream_t s);
+
+// Grouped bf16 GEMM: for g < G, y_g[m][n] = sum_k x_g[m][k] * w_g[n][k] with
+// x_g = x + g*gx (row stride sx), w_g = w + g*gw (rows of K), y_g = y + g*gy
+// (row stride sy); all in elements.
+struct Bf16GemmArgs {
+    int64_t G, M, N, K;
+    const uint16_t* x;
+    const uint16_t* w;
+    uint16_t* y;
+    int64_t sx, sy, gx, gw, gy;
+};
+hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t s);
+
 struct DenseGemmArgs {
     int64_t M, N, K;
     const uint16_t* x;  // bf16 [M][K]

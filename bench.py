@@ -120,6 +120,123 @@ def copy_calibration(torch, dev, mib: int) -> int:
     return 0
 
 
+def bench_bf16(args, w, torch, ap, wl, dev) -> int:
+    """The unquantised variant: oproj_inv_rope_bf16 then oproj_grouped_wo_a_bf16
+    (bf16 weights), timed the same way as the quantised path."""
+    if w.prequantised:
+        log("the pre-quantised workload has no unquantised form")
+        return 2
+    log(f"unquantised path, workload {w.name}: T={w.T} G={w.n_groups} hpg={w.heads_per_group} D={w.D} "
+        f"R={w.o_lora_rank}")
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    wq = wl.wo_a_bf16(w)
+    per_copy = wq.nbytes + 2 * o.nbytes
+    copies = args.copies or max(2, min(16, int(np.ceil(768e6 / per_copy))))
+    log(f"{copies} rotating copies of {per_copy / 1e6:.1f} MB")
+    shp = ap.Shape(T=w.T, n_groups=w.n_groups, heads_per_group=w.heads_per_group,
+                   o_lora_rank=w.o_lora_rank, max_pos=w.max_pos)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    d_tab, d_pos = t(tab), t(pos)
+    C = []
+    for _ in range(copies):
+        C.append({"o": t(o.view(np.int16)), "w": t(wq.view(np.int16)),
+                  "x": torch.empty((w.T, w.n_groups, w.D), dtype=torch.int16, device=dev),
+                  "z": torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=dev)})
+    torch.cuda.synchronize()
+
+    def rope(c):
+        ap.oproj_inv_rope_bf16(shp, c["o"], d_pos, d_tab, c["x"])
+
+    def gemm(c):
+        ap.oproj_grouped_wo_a_bf16(shp, c["x"], None, c["w"], c["z"])
+
+    def step(c):
+        rope(c)
+        gemm(c)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in C:
+                fn(c)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for c in C:
+                fn(c)
+        torch.cuda.synchronize()
+        return g
+
+    step(C[0])
+    torch.cuda.synchronize()
+    eager = C[0]["z"].clone()
+    g_step, g_rope, g_gemm = capture(step), capture(rope), capture(gemm)
+    g_step.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(C[0]["z"], eager):
+        log("graph replay differs from the eager result")
+        return 1
+    reps = max(1, args.steps // copies)
+    K = reps * copies
+    for _ in range(max(1, args.warmup // copies)):
+        g_step.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g_step.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+
+    def kernel_time_us(g):
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.kernel_reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (args.kernel_reps * copies)
+
+    t_rope, t_gemm = kernel_time_us(g_rope), kernel_time_us(g_gemm)
+    log(f"{K} steps: {ms_per_step * 1e3:.2f} us/step; kernel averages: rope {t_rope:.2f} us, "
+        f"grouped bf16 gemm {t_gemm:.2f} us")
+    G, R, D, T = w.n_groups, w.o_lora_rank, w.D, w.T
+    rope_bytes = 2 * T * w.H * 512 * 2 + T * 8 + T * 64 * 4
+    gemm_bytes = G * R * D * 2 + T * G * D * 2 + T * G * R * 2
+    gemm_flops = 2 * T * G * R * D
+    hbm_bound = gemm_flops / gemm_bytes < BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+    kernels = {"inv_rope_bf16": {"us": t_rope, "bound": "hbm", "bytes": rope_bytes,
+                                 "GB/s": rope_bytes / (t_rope * 1e3)},
+               "grouped_wo_a_bf16": {"us": t_gemm, "bound": "hbm" if hbm_bound else "mfma",
+                                     "bytes": gemm_bytes, "flops": gemm_flops,
+                                     "GB/s": gemm_bytes / (t_gemm * 1e3), "TFLOP/s": gemm_flops / (t_gemm * 1e6)}}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    kd = kernels[dom]
+    if kd["bound"] == "hbm":
+        achieved, peak, unit = kd["GB/s"], HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = kd["TFLOP/s"], BF16_PEAK_TFLOPS, "TFLOP/s"
+    result = {
+        "metric": "tokens/s of the unquantised path (bf16 inverse RoPE + grouped bf16 wo_a)",
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": max(1, args.warmup // copies) * copies, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 normals; random-init weights)",
+        "config": {"workload": f"{w.name} unquantised: T={T} n_groups={G} heads_per_group={w.heads_per_group} "
+                               f"D={D} o_lora_rank={R}", "global_batch": T, "parallelism": "single GPU",
+                   "copies_rotated": copies},
+        "roofline": {"bound": kd["bound"], "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": None},
+        "cpu_baseline": None,
+        "kernels": kernels,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap_ = argparse.ArgumentParser()
     ap_.add_argument("--gpus", type=int, default=1)
@@ -130,6 +247,8 @@ def main() -> int:
     ap_.add_argument("--kernel-reps", type=int, default=50, help="graph replays per kernel timing")
     ap_.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
     ap_.add_argument("--no-cpu-baseline", action="store_true")
+    ap_.add_argument("--path", default="fp8", choices=["fp8", "bf16"],
+                     help="fp8: the quantised path (default); bf16: the unquantised variant")
     ap_.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                      help="only run plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap_.parse_args()
@@ -152,6 +271,8 @@ def main() -> int:
         return copy_calibration(torch, dev, args.copy_calibration)
     ap.load_library()
     w = wl.WORKLOADS[args.workload]
+    if args.path == "bf16":
+        return bench_bf16(args, w, torch, ap, wl, dev)
     log(f"workload {w.name}: T={w.T} G={w.n_groups} hpg={w.heads_per_group} D={w.D} R={w.o_lora_rank}")
 
     # ---------------------------------------------------------------- inputs

@@ -1,7 +1,8 @@
 /*
  * oproj.h -- C ABI of the MI355X (gfx950) O-projection front half:
  *   inverse RoPE -> 1x128 block FP8 e4m3fn quantisation -> grouped wo_a GEMM
- *   [-> dense wo_b GEMM].
+ *   [-> dense wo_b GEMM], and the unquantised variant (bf16 inverse RoPE ->
+ *   grouped bf16 wo_a GEMM).
  *
  * Sources (web pages; cited by page title and section):
  *  [FUSED] vLLM API page "vllm.models.deepseek_v4.common.ops.fused_inv_rope_fp8_quant",
@@ -142,6 +143,44 @@ oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, co
  *  at most 4 GiB (M*K*2 and N*K*2 bytes), else OPROJ_E_SHAPE. */
 oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* x, const void* w,
                                    void* y, void* stream);
+
+/* Layout of a bf16 activation operand of the unquantised path, element strides:
+ *  x(t, g, k) at x[t*stride_t + g*stride_g + k],  k < D.
+ * Passing NULL selects token-major [T][G][D] (stride_t = G*D, stride_g = D),
+ * the [num_tokens, n_groups, group_dim] tensor [GWA] grouped_input returns
+ * (the same memory order as o).  Both strides must be multiples of 8
+ * (16 bytes) and non-negative. */
+typedef struct oproj_bf16_layout {
+    int64_t stride_t, stride_g;
+} oproj_bf16_layout;
+
+/* Step a1 without quantisation ([GWA] grouped_input: the fused kernel with
+ * quantize=False): the bf16 inverse-rotated groups.  For every token t and
+ * head h (group g = h / hpg, offset j = (h % hpg)*512):
+ *     x(t, g, j + k) = o[t][h][k]                      for k < 448 (copied)
+ *     rotated pair i of the last 64 dims as in oproj_inv_rope_quant
+ *     (e' = fma(d, s, e*c), d' = fma(-e, s, d*c) in fp32), rounded to bf16,
+ *     nearest even.
+ *  o          bf16 [T][H][512], contiguous;  positions int64 [T]
+ *  cos_sin    fp32 [max_pos][64]
+ *  x          bf16, layout `x_layout` (NULL: token-major [T][G][D])
+ * o_lora_rank is not used.  A position outside [0, max_pos) writes NaN into
+ * that token's 64 rotated dims of every head. */
+oproj_status oproj_inv_rope_bf16(const oproj_shape* shape, const void* o, const int64_t* positions,
+                                 const float* cos_sin, void* x, const oproj_bf16_layout* x_layout,
+                                 void* stream);
+
+/* Step a3 without quantisation ([OPROJ] deep_gemm_fp8_o_proj without FP8: a
+ * batched matmul of the bf16 groups with wo_a viewed [G, R, D]; [GWA]):
+ *   z[t][g][n] = sum_k x(t, g, k) * w[g*R + n][k],
+ * bf16 inputs, fp32 accumulation, one bf16 rounding (nearest even).
+ *  x   bf16 in layout `x_layout` (NULL: token-major [T][G][D])
+ *  w   bf16 [G*R][D] row-major;  z bf16 [T][G][R]
+ * Per group the activation rows must span at most 4 GiB ((T-1)*stride_t*2 +
+ * D*2 bytes), and so must the group's R weight rows; else OPROJ_E_SHAPE. */
+oproj_status oproj_grouped_wo_a_bf16(const oproj_shape* shape, const void* x,
+                                     const oproj_bf16_layout* x_layout, const void* w, void* z,
+                                     void* stream);
 
 /* Bytes of caller-provided workspace oproj_fused needs: the FP8 codes, the
  * scales and, when hidden > 0, the bf16 z; each region 256-byte aligned. */

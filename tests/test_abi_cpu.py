@@ -30,7 +30,8 @@ def _declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = _declared_symbols()
-    for s in ("oproj_inv_rope_quant", "oproj_grouped_wo_a", "oproj_fused",
+    for s in ("oproj_inv_rope_quant", "oproj_grouped_wo_a", "oproj_fused", "oproj_inv_rope_bf16",
+              "oproj_grouped_wo_a_bf16",
               "oproj_fused_workspace_bytes", "oproj_dense_bf16_gemm", "oproj_quantize_weight",
               "oproj_status_string", "oproj_version"):
         assert s in syms
@@ -111,6 +112,41 @@ def test_dense_gemm_validation(lib):
     assert f(4, 1 << 17, 1 << 15) == E_SHAPE  # weight operand beyond 4 GiB
     assert f(4, 16, 64, x=None) == E_NULL
     assert f(4, 16, 64, y=BAD) == E_ALIGN
+
+
+def _rb(shape, ptrs=(0x1000,) * 4, layout=None):
+    o, pos, tab, x = ptrs
+    return _raw("oproj_inv_rope_bf16", ctypes.byref(shape._c()), o, pos, tab, x,
+                ctypes.byref(layout._c()) if layout else None, None)
+
+
+def _gb(shape, ptrs=(0x1000,) * 3, layout=None):
+    x, w, z = ptrs
+    return _raw("oproj_grouped_wo_a_bf16", ctypes.byref(shape._c()), x,
+                ctypes.byref(layout._c()) if layout else None, w, z, None)
+
+
+def test_inv_rope_bf16_validation(lib):
+    assert _rb(_shape(T=0), ptrs=(None,) * 4) == E_OK
+    assert _rb(_shape(T=-2)) == E_SHAPE
+    assert _rb(_shape(nope_dim=960, rope_dim=64)) == E_MODE
+    assert _rb(_shape(heads_per_group=3)) == E_MODE
+    assert _rb(_shape(), ptrs=(0x1000, None, 0x1000, 0x1000)) == E_NULL
+    assert _rb(_shape(), ptrs=(0x1000, 0x1000, 0x1000, BAD)) == E_ALIGN
+    assert _rb(_shape(), ptrs=(0x1000, 0x1004, 0x1000, 0x1000)) == E_ALIGN  # int64 positions
+    assert _rb(_shape(), layout=_native.Bf16Layout(1020, 8)) == E_ALIGN
+    assert _rb(_shape(), layout=_native.Bf16Layout(1024, -8)) == E_SHAPE
+
+
+def test_grouped_wo_a_bf16_validation(lib):
+    assert _gb(_shape(T=0), ptrs=(None,) * 3) == E_OK
+    assert _gb(_shape(o_lora_rank=96)) == E_SHAPE
+    assert _gb(_shape(heads_per_group=3)) == E_MODE
+    assert _gb(_shape(), ptrs=(0x1000, None, 0x1000)) == E_NULL
+    assert _gb(_shape(), ptrs=(0x1000, 0x1000, BAD)) == E_ALIGN
+    assert _gb(_shape(), layout=_native.Bf16Layout(4, 8)) == E_ALIGN
+    # a group's activation rows beyond 4 GiB
+    assert _gb(_shape(T=1 << 20), layout=_native.Bf16Layout(4096, 1024)) == E_SHAPE
 
 
 def test_fused_workspace_and_validation(lib):

@@ -292,6 +292,12 @@ def wo_a_f32(w: Workload) -> np.ndarray:
         w.n_groups * w.o_lora_rank, w.D)
 
 
+def wo_a_bf16(w: Workload) -> np.ndarray:
+    """bf16 bit patterns [G*R, D] of an unquantised wo_a: the fp32 weight of
+    wo_a_f32 rounded to bf16 (nearest even)."""
+    return f32_to_bf16_bits(wo_a_f32(w))
+
+
 def wo_b_bf16(w: Workload) -> np.ndarray:
     """bf16 bit patterns [hidden, G*R] of wo_b, N(0, 0.02^2)."""
     n = w.hidden * w.n_groups * w.o_lora_rank
