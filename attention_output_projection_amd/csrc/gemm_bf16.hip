@@ -188,6 +188,122 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Few-token kernel (M <= 128): the weight stream is the cost, so the tile is
+// 64 rows x 64 columns (no rows computed for nothing) and, as in the FP8
+// decode kernel, the eight waves form two K-groups of four that each walk
+// half of K through their own ring of XNS steps (XNS-1 in flight), one
+// 64-element step (128 bytes of every row) per s_waitcnt + barrier.  In a
+// K-group waves 0-1 copy (weights with the non-temporal hint: read once)
+// and all four compute, wave w owning columns 16w..16w+15.  The K-groups'
+// fp32 partial tiles are summed through LDS and stored as whole rows.
+constexpr int XBM = 64, XBN = 64, XNS = 4, XKS = 2;
+constexpr int XSTAGE = 64 * 128 * 2;  // activation slab + weight slab
+constexpr int XVM = 8;                // copy instructions per copying wave per step
+constexpr int XPROW = XBN + 4;        // fp32 per row of an epilogue partial tile
+static_assert(XKS * XBM * XPROW * 4 <= XKS * XNS * XSTAGE, "the epilogue fits in the ring");
+
+__global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[XKS][XNS][XSTAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group
+    const bool copier = wave < 2;
+    const int64_t per = p.mtiles * p.ntiles;
+    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per);
+    const int64_t g = gid / per, id = gid - g * per;
+    const int64_t m0 = (id / p.ntiles) * XBM, n0 = (id % p.ntiles) * XBN;
+    const int64_t kbytes = p.K * 2, xrow = p.sx * 2;
+    const int64_t nstep = kbytes / 128;
+    const int64_t s0 = nstep * kq / XKS, ns = nstep * (kq + 1) / XKS - s0;
+
+    // copy plan: copying wave c moves rows 32c..32c+31 of both slabs, 8 rows
+    // of 128 bytes per instruction
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x + g * p.gx);
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.w + g * p.gw);
+    uint32_t aoff[4], woff[4];
+    if (copier) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 32 * wave + 8 * j + (lane >> 3);
+            const int piece = (lane & 7) ^ swz(row);
+            int64_t m = m0 + row;
+            m = m < p.M ? m : p.M - 1;  // rows past M are computed but never stored
+            aoff[j] = (uint32_t)(m * xrow + piece * 16);
+            int64_t n = n0 + row;
+            n = n < p.N ? n : p.N - 1;
+            woff[j] = (uint32_t)(n * kbytes + piece * 16);
+        }
+    }
+    const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
+    auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
+        const int64_t ks = s0 + i;
+        const uint32_t st = ring0 + (uint32_t)(slot * XSTAGE);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16s(xb + ks * 128, aoff[j], st + (32 * wave + 8 * j) * 128);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16s_nt(wb + ks * 128, woff[j], st + 8192 + (32 * wave + 8 * j) * 128);
+    };
+    if (copier) {
+#pragma unroll
+        for (int s = 0; s < XNS - 1; ++s)
+            if (s < ns) issue(s, s);
+    }
+
+    v4f acc[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) acc[mi] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int frow = lane & 15;
+    const int p0 = 2 * (lane >> 4);
+    const int64_t nst = (nstep + XKS - 1) / XKS;  // the largest share: same barrier count in both groups
+    for (int64_t i = 0; i < nst; ++i) {
+        if (copier) wait_ahead<XNS - 2, XVM>(ns - 1 - i);
+        __builtin_amdgcn_s_barrier();
+        if (copier && i + XNS - 1 < ns) issue(i + XNS - 1, (int)((i + XNS - 1) % XNS));
+        if (i >= ns) continue;  // uniform per K-group
+        const uint8_t* st = ring[kq][i % XNS];
+        const int rb = 16 * wave + frow;
+        const v8bf blo = *reinterpret_cast<const v8bf*>(st + 8192 + rb * 128 + 16 * (p0 ^ swz(rb)));
+        const v8bf bhi = *reinterpret_cast<const v8bf*>(st + 8192 + rb * 128 + 16 * ((p0 + 1) ^ swz(rb)));
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int r = 16 * mi + frow;
+            const v8bf alo = *reinterpret_cast<const v8bf*>(st + r * 128 + 16 * (p0 ^ swz(r)));
+            const v8bf ahi = *reinterpret_cast<const v8bf*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
+            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo, acc[mi], 0, 0, 0);
+            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[mi], 0, 0, 0);
+        }
+    }
+    wait_vmcnt<0>();  // (already true: the last step was waited for in full)
+    __syncthreads();
+
+    float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [XKS][64][XPROW]
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            part[(kq * XBM + 16 * mi + 4 * (lane >> 4) + i) * XPROW + 16 * wave + frow] = acc[mi][i];
+    __syncthreads();
+    for (int idx = tid; idx < XBM * (XBN / 8); idx += XKS * 256) {
+        const int r = idx / (XBN / 8), ch = idx % (XBN / 8);
+        float4 s0v = *reinterpret_cast<const float4*>(part + r * XPROW + 8 * ch);
+        float4 s1v = *reinterpret_cast<const float4*>(part + r * XPROW + 8 * ch + 4);
+#pragma unroll
+        for (int q = 1; q < XKS; ++q) {
+            const float4 u0 = *reinterpret_cast<const float4*>(part + (q * XBM + r) * XPROW + 8 * ch);
+            const float4 u1 = *reinterpret_cast<const float4*>(part + (q * XBM + r) * XPROW + 8 * ch + 4);
+            s0v.x += u0.x; s0v.y += u0.y; s0v.z += u0.z; s0v.w += u0.w;
+            s1v.x += u1.x; s1v.y += u1.y; s1v.z += u1.z; s1v.w += u1.w;
+        }
+        const uint4 v = {f32_to_bf16_bits(s0v.x) | (f32_to_bf16_bits(s0v.y) << 16),
+                         f32_to_bf16_bits(s0v.z) | (f32_to_bf16_bits(s0v.w) << 16),
+                         f32_to_bf16_bits(s1v.x) | (f32_to_bf16_bits(s1v.y) << 16),
+                         f32_to_bf16_bits(s1v.z) | (f32_to_bf16_bits(s1v.w) << 16)};
+        const int64_t row = m0 + r, col = n0 + 8 * ch;
+        if (row < p.M && col < p.N) *reinterpret_cast<uint4*>(p.y + g * p.gy + row * p.sy + col) = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
@@ -204,6 +320,13 @@ hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
     p.gw = a.gw;
     p.gy = a.gy;
     p.G = a.G;
+    if (a.M <= 128) {  // few tokens: 64x64 tiles, K split over two wave groups
+        p.mtiles = (a.M + XBM - 1) / XBM;
+        p.ntiles = (a.N + XBN - 1) / XBN;
+        hipLaunchKernelGGL(gemm_bf16_decode_kernel, dim3((unsigned)(a.G * p.mtiles * p.ntiles)),
+                           dim3(XKS * 256), 0, stream, p);
+        return hipGetLastError();
+    }
     p.mtiles = (a.M + BM - 1) / BM;
     // 64-column tiles when 256-column tiles leave most of the chip idle;
     // otherwise 224-column tiles when they fill the last round of 256

@@ -297,21 +297,6 @@ constexpr int DVM = 9;  // copy instructions per copying wave per stage
 constexpr int DPROW = DBN + 4;  // fp32 per row of an epilogue partial tile (pad against bank conflicts)
 static_assert(DKS * DBM * DPROW * 4 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
 
-// Wait until at most min(ahead, N) stages of this wave's copies are still in
-// flight (ahead < 0 counts as 0): the stage being waited for is followed by
-// `ahead` issued stages.
-template <int N>
-__device__ __forceinline__ void wait_stage(int64_t ahead) {
-    if constexpr (N == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (ahead >= N)
-            wait_vmcnt<DVM * N>();
-        else
-            wait_stage<N - 1>(ahead);
-    }
-}
-
 // One workgroup's output tile (the whole decode pipeline); ring is the
 // workgroup's LDS.
 template <bool MX, bool W1>
@@ -398,7 +383,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         // this wave's copies of stage i have landed; the copies of the stages
         // after it that were issued (at most DNS-2, none past the group's
         // last block) may still be in flight
-        if (copier) wait_stage<DNS - 2>(nkb - 1 - i);
+        if (copier) wait_ahead<DNS - 2, DVM>(nkb - 1 - i);
         __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence)
         if (copier && i + DNS - 1 < nkb) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
         if (i >= nkb) continue;        // uniform per wave group

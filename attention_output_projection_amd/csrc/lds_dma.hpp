@@ -42,6 +42,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait until at most min(ahead, N) pipeline steps of this wave's copies are
+// still in flight, PER copy instructions per step (ahead < 0 counts as 0):
+// the step being waited for is followed by `ahead` issued steps.
+template <int N, int PER>
+__device__ __forceinline__ void wait_ahead(int64_t ahead) {
+    if constexpr (N <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= N)
+            wait_vmcnt<PER * N>();
+        else
+            wait_ahead<N - 1, PER>(ahead);
+    }
+}
+
 // 16-byte piece swizzle of a 128-byte LDS row.  A fragment read (ds_read_b128)
 // has the lanes of 16 consecutive rows fetch the same piece; XOR with
 // (row & 7) ^ ((row >> 3) & 1) puts any 8 consecutive rows on 8 different

@@ -9,12 +9,12 @@
 // x(t, g, (h % hpg)*512 + k) = o(t, h, k) for k < 448; the 64 RoPE dims of
 // each head are rotated by -theta with the same fp32 operation order as the
 // quantising kernel (e' = fma(d, s, e*c), d' = fma(-e, s, d*c)) and rounded
-// to bf16, nearest even.  Work unit: one wave per head row (t, h); lane l
-// moves elements 8l..8l+7 (one 16-byte non-temporal load and store), lanes
-// 56..63 hold the RoPE dims and fetch cos[4(l-56)..+3], sin[..] of the
-// token's position.  Items are numbered in address order and dealt
-// round-robin over a fixed population of waves, each of which loads its next
-// row while it stores the current one.  HBM-bound: 1 KiB read + 1 KiB
+// to bf16, nearest even.  Work unit: one wave per four consecutive head rows;
+// lane l moves elements 8l..8l+7 of each (16-byte non-temporal loads and
+// stores), lanes 56..63 hold the RoPE dims and fetch cos[4(l-56)..+3],
+// sin[..] of each row's token position.  Items are numbered in address order
+// and dealt round-robin over a fixed population of waves, each of which loads
+// its next item while it stores the current one.  HBM-bound: 1 KiB read + 1 KiB
 // written per head row.  A position outside [0, max_pos) writes NaN into the
 // token's RoPE dims.
 #include "device_common.hpp"
@@ -35,50 +35,67 @@ struct RBParams {
     const int64_t* pos;
     const float* table;
     uint16_t* x;
-    int64_t H, hpg, max_pos, nitems, st, sg;
+    int64_t H, hpg, max_pos, nrows, nitems, st, sg;
 };
 
-struct RbRow {
-    rb_u32x4 raw;
-    float4 cs, sn;
-    bool bad;
+constexpr int kRbRows = 4;  // head rows per work item (4 KiB read per wave in flight)
+
+struct RbItem {
+    rb_u32x4 raw[kRbRows];
+    float4 cs[kRbRows], sn[kRbRows];
+    bool bad[kRbRows];
 };
 
-__device__ __forceinline__ RbRow rb_load(const RBParams& p, int64_t item, int lane) {
-    item = item < p.nitems ? item : p.nitems - 1;  // kept in bounds; never stored
-    RbRow r;
-    r.raw = __builtin_nontemporal_load(reinterpret_cast<const rb_u32x4*>(p.o + item * 512 + 8 * lane));
-    const int64_t ps = p.pos[item / p.H];
-    r.bad = (ps < 0) | (ps >= p.max_pos);
-    r.cs = make_float4(1.f, 1.f, 1.f, 1.f);
-    r.sn = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane >= 56 && !r.bad) {
-        const float* row = p.table + ps * 64 + 4 * (lane - 56);
-        r.cs = *reinterpret_cast<const float4*>(row);
-        r.sn = *reinterpret_cast<const float4*>(row + 32);
+// rows past the end load the last row (kept in bounds) and are never stored
+__device__ __forceinline__ RbItem rb_load(const RBParams& p, int64_t item, int lane) {
+    RbItem r;
+#pragma unroll
+    for (int j = 0; j < kRbRows; ++j) {
+        int64_t row = item * kRbRows + j;
+        row = row < p.nrows ? row : p.nrows - 1;
+        r.raw[j] = __builtin_nontemporal_load(reinterpret_cast<const rb_u32x4*>(p.o + row * 512 + 8 * lane));
+    }
+#pragma unroll
+    for (int j = 0; j < kRbRows; ++j) {
+        int64_t row = item * kRbRows + j;
+        row = row < p.nrows ? row : p.nrows - 1;
+        const int64_t ps = p.pos[row / p.H];
+        r.bad[j] = (ps < 0) | (ps >= p.max_pos);
+        r.cs[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+        r.sn[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lane >= 56 && !r.bad[j]) {
+            const float* trow = p.table + ps * 64 + 4 * (lane - 56);
+            r.cs[j] = *reinterpret_cast<const float4*>(trow);
+            r.sn[j] = *reinterpret_cast<const float4*>(trow + 32);
+        }
     }
     return r;
 }
 
-__device__ __forceinline__ void rb_store(const RBParams& p, int64_t item, int lane, const RbRow& r) {
-    rb_u32x4 out = r.raw;
-    if (lane >= 56) {
-        const uint32_t w4[4] = {r.raw.x, r.raw.y, r.raw.z, r.raw.w};
-        const float cc[4] = {r.cs.x, r.cs.y, r.cs.z, r.cs.w};
-        const float ss[4] = {r.sn.x, r.sn.y, r.sn.z, r.sn.w};
-        uint32_t o4[4];
+__device__ __forceinline__ void rb_store(const RBParams& p, int64_t item, int lane, const RbItem& r) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float e = bf16_lo(w4[m]), d = bf16_hi(w4[m]);
-            const float e2 = __builtin_fmaf(d, ss[m], e * cc[m]);
-            const float d2 = __builtin_fmaf(-e, ss[m], d * cc[m]);
-            o4[m] = r.bad ? 0x7FC07FC0u : (f32_to_bf16_bits(e2) | (f32_to_bf16_bits(d2) << 16));
+    for (int j = 0; j < kRbRows; ++j) {
+        const int64_t row = item * kRbRows + j;
+        if (row >= p.nrows) break;
+        rb_u32x4 out = r.raw[j];
+        if (lane >= 56) {
+            const uint32_t w4[4] = {r.raw[j].x, r.raw[j].y, r.raw[j].z, r.raw[j].w};
+            const float cc[4] = {r.cs[j].x, r.cs[j].y, r.cs[j].z, r.cs[j].w};
+            const float ss[4] = {r.sn[j].x, r.sn[j].y, r.sn[j].z, r.sn[j].w};
+            uint32_t o4[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float e = bf16_lo(w4[m]), d = bf16_hi(w4[m]);
+                const float e2 = __builtin_fmaf(d, ss[m], e * cc[m]);
+                const float d2 = __builtin_fmaf(-e, ss[m], d * cc[m]);
+                o4[m] = r.bad[j] ? 0x7FC07FC0u : (f32_to_bf16_bits(e2) | (f32_to_bf16_bits(d2) << 16));
+            }
+            out = rb_u32x4{o4[0], o4[1], o4[2], o4[3]};
         }
-        out = rb_u32x4{o4[0], o4[1], o4[2], o4[3]};
+        const int64_t t = row / p.H, h = row % p.H, g = h / p.hpg;
+        uint16_t* dst = p.x + t * p.st + g * p.sg + (h % p.hpg) * 512 + 8 * lane;
+        __builtin_nontemporal_store(out, reinterpret_cast<rb_u32x4*>(dst));
     }
-    const int64_t t = item / p.H, h = item % p.H, g = h / p.hpg;
-    uint16_t* dst = p.x + t * p.st + g * p.sg + (h % p.hpg) * 512 + 8 * lane;
-    __builtin_nontemporal_store(out, reinterpret_cast<rb_u32x4*>(dst));
 }
 
 __global__ __launch_bounds__(kRbWaves * 64) void inv_rope_bf16_kernel(RBParams p) {
@@ -87,9 +104,9 @@ __global__ __launch_bounds__(kRbWaves * 64) void inv_rope_bf16_kernel(RBParams p
     const int64_t nwaves = (int64_t)gridDim.x * kRbWaves;
     const int64_t first = (int64_t)blockIdx.x * kRbWaves + wave;
     if (first >= p.nitems) return;
-    RbRow next = rb_load(p, first, lane);
+    RbItem next = rb_load(p, first, lane);
     for (int64_t item = first; item < p.nitems; item += nwaves) {
-        const RbRow cur = next;
+        const RbItem cur = next;
         if (item + nwaves < p.nitems) next = rb_load(p, item + nwaves, lane);
         rb_store(p, item, lane, cur);
     }
@@ -98,7 +115,7 @@ __global__ __launch_bounds__(kRbWaves * 64) void inv_rope_bf16_kernel(RBParams p
 }  // namespace
 
 #ifndef OPROJ_RB_WAVES_PER_CU
-#define OPROJ_RB_WAVES_PER_CU 12
+#define OPROJ_RB_WAVES_PER_CU 16
 #endif
 
 hipError_t launch_inv_rope_bf16(const RopeBf16Args& a, hipStream_t stream) {
@@ -110,7 +127,8 @@ hipError_t launch_inv_rope_bf16(const RopeBf16Args& a, hipStream_t stream) {
     p.H = a.G * a.hpg;
     p.hpg = a.hpg;
     p.max_pos = a.max_pos;
-    p.nitems = a.T * p.H;
+    p.nrows = a.T * p.H;
+    p.nitems = (p.nrows + kRbRows - 1) / kRbRows;
     p.st = a.stride_t;
     p.sg = a.stride_g;
     int64_t waves = 256 * OPROJ_RB_WAVES_PER_CU;
