@@ -62,6 +62,10 @@ def _load():
                                          I64, P, I64, P, INT]
         lib.orc_dense_gemm_bf16.argtypes = [I64, I64, I64, P, P, P, I64, P, INT]
         lib.orc_inv_rope_bf16.argtypes = [I64, I64, I64, I64, P, P, P, P]
+        lib.orc_e8m0_byte.argtypes = [ctypes.c_float]
+        lib.orc_e8m0_byte.restype = INT
+        lib.orc_e8m0_pack.argtypes = [I64, I64, P, P]
+        lib.orc_e8m0_pack.restype = INT
         for f in (lib.orc_rope_f32, lib.orc_block_quant_rows, lib.orc_inv_rope_quant,
                   lib.orc_quant_weight, lib.orc_grouped_gemm, lib.orc_dense_gemm_bf16,
                   lib.orc_inv_rope_bf16):
@@ -171,6 +175,19 @@ def inv_rope_quant(o_bf16, positions, table, n_groups: int, heads_per_group: int
                                _p(o), _p(pos), _p(tab), _p(q), _p(s),
                                nthreads or default_threads())
     return q, s
+
+
+def e8m0_pack(scales) -> np.ndarray:
+    """Power-of-two fp32 scales [..., n] (n % 4 == 0) -> packed UE8M0 words
+    [..., n/4], uint32; block 4j+b in byte b of word j."""
+    s = _c(scales, np.float32)
+    n = s.shape[-1]
+    assert n % 4 == 0
+    rows = s.size // n
+    w = np.empty(s.shape[:-1] + (n // 4,), np.uint32)
+    if _load().orc_e8m0_pack(rows, n, _p(s), _p(w)) != 0:
+        raise ValueError("a scale is not a power of two representable in UE8M0")
+    return w
 
 
 def quant_weight(w, block_rows: int = 128, pow2: bool = False):

@@ -43,6 +43,11 @@
  *      fp32 -> bf16 to nearest even; dims 0..nope-1 are copied unchanged.  The
  *      grouped bf16 contraction ([OPROJ] deep_gemm_fp8_o_proj without FP8:
  *      one matmul per group) accumulates in fp64.
+ *  R10 packed UE8M0 scales ([OPROJ] rope_quant_attn_out and
+ *      compute_fp8_einsum_recipe: one int32 per head over its four 128-wide
+ *      blocks, MN-major): the byte of a power-of-two scale 2^k is k + 127 (an
+ *      unsigned biased exponent, no mantissa); NaN is 0xFF; block 4j+b of the
+ *      row sits in bits 8b..8b+7 of word j (the four bytes in memory order).
  */
 #include <math.h>
 #include <pthread.h>
@@ -473,6 +478,36 @@ void orc_dense_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* x, con
         pthread_create(&th[i], NULL, orc_dense_worker, &jobs[i]);
     }
     for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
+/* UE8M0 byte of one scale (R10): the biased exponent of a power of two,
+ * found by halving/doubling in exact fp64 arithmetic (no bit tricks); 0xFF
+ * for NaN; -1 if the value is not a positive power of two in [2^-127, 2^127]. */
+int orc_e8m0_byte(float s) {
+    if (isnan(s)) return 0xFF;
+    double v = (double)s;
+    if (!(v > 0.0)) return -1;
+    int k = 0;
+    while (v >= 2.0) { v /= 2.0; ++k; }
+    while (v < 1.0) { v *= 2.0; --k; }
+    if (v != 1.0 || k < -127 || k > 127) return -1;
+    return k + 127;
+}
+
+/* Pack rows of n scales (n % 4 == 0) into n/4 words per row (R10).
+ * Returns 0, or -1 when some scale has no UE8M0 byte. */
+int orc_e8m0_pack(int64_t rows, int64_t n, const float* s, uint32_t* w) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < n / 4; ++j) {
+            uint32_t word = 0;
+            for (int b = 0; b < 4; ++b) {
+                int e = orc_e8m0_byte(s[r * n + 4 * j + b]);
+                if (e < 0) return -1;
+                word |= (uint32_t)e << (8 * b);
+            }
+            w[r * (n / 4) + j] = word;
+        }
+    return 0;
 }
 
 /* Array helpers for the Python side (vectorised codecs). */

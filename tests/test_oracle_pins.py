@@ -525,6 +525,40 @@ def test_dense_bf16_gemm_matches_numpy():
     assert np.array_equal(oracle.dense_gemm_bf16(x, w, idx=idx), y[idx[:, 0], idx[:, 1]])
 
 
+# ---------------------------------------------------------------- packed UE8M0 scales
+def test_e8m0_pack_matches_torch_e8m0_codec():
+    """Library route: torch's float8_e8m0fnu stores a power of two as its
+    biased exponent byte; bytes land in memory order inside each word."""
+    rng = np.random.default_rng(41)
+    k = rng.integers(-127, 128, (5, 3, 8))
+    s = np.ldexp(np.ones(k.shape), k).astype(np.float32)
+    w = oracle.e8m0_pack(s)
+    assert w.shape == (5, 3, 2) and w.dtype == np.uint32
+    tb = torch.from_numpy(s.reshape(-1)).to(torch.float8_e8m0fnu).view(torch.uint8).numpy()
+    assert np.array_equal(w.reshape(-1).view(np.uint8), tb)  # little-endian words = byte order
+    assert np.array_equal(w.view(np.uint8).reshape(5, 3, 8).astype(np.int64) - 127, k)
+
+
+def test_e8m0_pack_nan_and_rejects():
+    s = np.array([[1.0, np.nan, 0.5, 2.0 ** 100]], np.float32)
+    w = oracle.e8m0_pack(s)
+    assert w.view(np.uint8).reshape(-1).tolist() == [127, 0xFF, 126, 227]
+    for bad in (3.0, 0.0, -2.0):
+        with pytest.raises(ValueError):
+            oracle.e8m0_pack(np.array([[1.0, 1.0, 1.0, bad]], np.float32))
+
+
+def test_e8m0_of_pow2_quant_scales_roundtrips():
+    """The pow2 recipe's scales are exact powers of two: every one packs, and
+    2^(byte-127) gives it back."""
+    o = wl.normal_bf16(42, 3 * 4 * 512).reshape(3, 4, 512)
+    tab = wl.cos_sin_table(4096, 64)
+    _, sc = oracle.inv_rope_quant(o, np.array([0, 9, 4000], np.int64), tab, 2, 2, pow2=True)
+    w = oracle.e8m0_pack(sc)
+    back = np.ldexp(1.0, w.view(np.uint8).astype(np.int64) - 127).reshape(sc.shape)
+    assert np.array_equal(back.astype(np.float32), sc)
+
+
 # ---------------------------------------------------------------- unquantised path
 def _bf16_rows(T, H, seed):
     return wl.normal_bf16(seed, T * H * 512).reshape(T, H, 512)
