@@ -10,6 +10,7 @@ library (``python -m attention_output_projection_amd.build``) and raises if it
 is missing.  There is no CPU fallback.
 """
 from ._native import (  # noqa: F401
+    OPROJ_SCALE_E8M0,
     OPROJ_SCALE_FP32,
     OPROJ_SCALE_POW2,
     OPROJ_WBLOCK_1x128,

@@ -12,6 +12,7 @@ _LIB_PATH = os.path.join(_HERE, "liboproj.so")
 
 OPROJ_SCALE_FP32 = 0
 OPROJ_SCALE_POW2 = 1
+OPROJ_SCALE_E8M0 = 2
 OPROJ_WBLOCK_128x128 = 0
 OPROJ_WBLOCK_1x128 = 1
 
@@ -88,9 +89,11 @@ class Bf16Layout:
         return _Bf16Layout(self.stride_t, self.stride_g)
 
 
-def default_layout(shape: Shape) -> ActLayout:
-    """Group-major codes [G][T][D] and MN-major scales [G][KB][T]."""
-    return ActLayout(shape.D, shape.T * shape.D, 1, shape.KB * shape.T, shape.T)
+def default_layout(shape: Shape, scale_mode: int = OPROJ_SCALE_FP32) -> ActLayout:
+    """Group-major codes [G][T][D] and MN-major scales [G][KB][T] ([G][KB/4][T]
+    packed UE8M0 words in OPROJ_SCALE_E8M0 mode)."""
+    nw = shape.KB // 4 if scale_mode == OPROJ_SCALE_E8M0 else shape.KB
+    return ActLayout(shape.D, shape.T * shape.D, 1, nw * shape.T, shape.T)
 
 
 _lib = None

@@ -33,8 +33,13 @@ oproj_status check_shape(const oproj_shape* s, bool need_rank) {
     return OPROJ_OK;
 }
 
-oproj::ActLayout default_layout(const oproj_shape* s) {
-    const int64_t D = s->heads_per_group * 512, KB = D / 128;
+bool valid_mode(int32_t m) {
+    return m == OPROJ_SCALE_FP32 || m == OPROJ_SCALE_POW2 || m == OPROJ_SCALE_E8M0;
+}
+
+// default layout; in UE8M0 mode a scale word covers four K-blocks
+oproj::ActLayout default_layout(const oproj_shape* s, int32_t mode) {
+    const int64_t D = s->heads_per_group * 512, KB = D / 128 / (mode == OPROJ_SCALE_E8M0 ? 4 : 1);
     oproj::ActLayout l;
     l.stride_t = D;
     l.stride_g = s->T * D;
@@ -53,8 +58,8 @@ oproj_status check_layout(const oproj_act_layout* l) {
     return OPROJ_OK;
 }
 
-oproj::ActLayout to_layout(const oproj_act_layout* l, const oproj_shape* s) {
-    if (!l) return default_layout(s);
+oproj::ActLayout to_layout(const oproj_act_layout* l, const oproj_shape* s, int32_t mode) {
+    if (!l) return default_layout(s, mode);
     oproj::ActLayout o;
     o.stride_t = l->stride_t;
     o.stride_g = l->stride_g;
@@ -90,11 +95,11 @@ namespace {
 
 // Validation + argument set-up of step a1+a2 (shared by the entry points).
 oproj_status prep_quant(const oproj_shape* shape, int32_t scale_mode, const void* o, const int64_t* positions,
-                        const float* cos_sin, void* a_codes, float* a_scales, const oproj_act_layout* out_layout,
+                        const float* cos_sin, void* a_codes, void* a_scales, const oproj_act_layout* out_layout,
                         oproj::RopeQuantArgs* a) {
     oproj_status st = check_shape(shape, false);
     if (st != OPROJ_OK) return st;
-    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
     if ((st = check_layout(out_layout)) != OPROJ_OK) return st;
     if (shape->T == 0) return OPROJ_OK;
     if (!o || !positions || !cos_sin || !a_codes || !a_scales) return OPROJ_E_NULL;
@@ -105,23 +110,24 @@ oproj_status prep_quant(const oproj_shape* shape, int32_t scale_mode, const void
     a->G = shape->n_groups;
     a->hpg = shape->heads_per_group;
     a->max_pos = shape->max_pos;
-    a->pow2 = scale_mode == OPROJ_SCALE_POW2;
+    a->pow2 = scale_mode != OPROJ_SCALE_FP32;
+    a->e8m0 = scale_mode == OPROJ_SCALE_E8M0;
     a->o = static_cast<const uint16_t*>(o);
     a->positions = positions;
     a->cos_sin = cos_sin;
     a->codes = static_cast<uint8_t*>(a_codes);
     a->scales = a_scales;
-    a->lay = to_layout(out_layout, shape);
+    a->lay = to_layout(out_layout, shape, scale_mode);
     return OPROJ_OK;
 }
 
 // Validation + argument set-up of step a3 (shared by the entry points).
-oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void* a_codes, const float* a_scales,
+oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void* a_codes, const void* a_scales,
                        const oproj_act_layout* a_layout, const void* w_codes, const float* w_scales,
                        int32_t w_block, void* z, oproj::GroupedGemmArgs* a) {
     oproj_status st = check_shape(shape, true);
     if (st != OPROJ_OK) return st;
-    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
     if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
     if ((st = check_layout(a_layout)) != OPROJ_OK) return st;
     if (shape->T == 0) return OPROJ_OK;
@@ -131,7 +137,7 @@ oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void*
         return OPROJ_E_ALIGN;
     {
         // the kernels address operands as a uniform base plus 32-bit lane offsets
-        const oproj::ActLayout l = to_layout(a_layout, shape);
+        const oproj::ActLayout l = to_layout(a_layout, shape, scale_mode);
         const int64_t D = shape->heads_per_group * 512, KB = D / 128, lim = int64_t(1) << 32;
         const int64_t rows = shape->n_groups * shape->o_lora_rank;
         if ((shape->T - 1) * l.stride_t + D >= lim || (shape->T - 1) * l.s_stride_t * 4 + 4 >= lim ||
@@ -142,11 +148,12 @@ oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void*
     a->G = shape->n_groups;
     a->D = shape->heads_per_group * 512;
     a->R = shape->o_lora_rank;
-    a->mx = scale_mode == OPROJ_SCALE_POW2;
+    a->mx = scale_mode != OPROJ_SCALE_FP32;
+    a->a_e8m0 = scale_mode == OPROJ_SCALE_E8M0;
     a->w_1x128 = w_block == OPROJ_WBLOCK_1x128;
     a->a = static_cast<const uint8_t*>(a_codes);
     a->sa = a_scales;
-    a->lay = to_layout(a_layout, shape);
+    a->lay = to_layout(a_layout, shape, scale_mode);
     a->w = static_cast<const uint8_t*>(w_codes);
     a->sw = w_scales;
     a->z = static_cast<uint16_t*>(z);
@@ -157,7 +164,7 @@ oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void*
 
 oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
                                   const int64_t* positions, const float* cos_sin, void* a_codes,
-                                  float* a_scales, const oproj_act_layout* out_layout,
+                                  void* a_scales, const oproj_act_layout* out_layout,
                                   void* stream) {
     oproj::RopeQuantArgs a;
     const oproj_status st = prep_quant(shape, scale_mode, o, positions, cos_sin, a_codes, a_scales, out_layout, &a);
@@ -166,7 +173,7 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
 }
 
 oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
-                                const float* a_scales, const oproj_act_layout* a_layout,
+                                const void* a_scales, const oproj_act_layout* a_layout,
                                 const void* w_codes, const float* w_scales, int32_t w_block,
                                 void* z, void* stream) {
     oproj::GroupedGemmArgs a;
@@ -284,7 +291,7 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
                          void* workspace, size_t workspace_bytes, void* out, void* stream) {
     oproj_status st = check_shape(shape, true);
     if (st != OPROJ_OK) return st;
-    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
     if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
     if (wo_b && (hidden < 16 || hidden % 16 != 0)) return OPROJ_E_SHAPE;
     if (shape->T == 0) return OPROJ_OK;
@@ -322,7 +329,7 @@ oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int
                                    const float* w, void* codes, float* scales, void* stream) {
     if (rows < 0 || K < 128 || K % 128 != 0) return OPROJ_E_SHAPE;
     if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
-    if (scale_mode != OPROJ_SCALE_FP32 && scale_mode != OPROJ_SCALE_POW2) return OPROJ_E_MODE;
+    if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
     if (rows == 0) return OPROJ_OK;
     if (!w || !codes || !scales) return OPROJ_E_NULL;
     if ((reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
@@ -331,7 +338,7 @@ oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int
     a.rows = rows;
     a.K = K;
     a.brows = w_block == OPROJ_WBLOCK_1x128 ? 1 : 128;
-    a.pow2 = scale_mode == OPROJ_SCALE_POW2;
+    a.pow2 = scale_mode != OPROJ_SCALE_FP32;  // weight scales stay fp32 powers of two in UE8M0 mode
     a.w = w;
     a.codes = static_cast<uint8_t*>(codes);
     a.scales = scales;

@@ -56,7 +56,17 @@ struct GParams {
     int64_t st, sg, sst, ssg, sskb;
     int64_t mtiles, ntiles;
     int w_shift;  // 7: 128x128 weight scales; 0: per row
+    int kshift;   // activation scale words hold 1 << kshift K-blocks (0: fp32, 2: packed UE8M0)
+    int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
 };
+
+// Exponent byte (E8M0) of activation scale word `raw` for K-block kb: the
+// exponent field of a power-of-two fp32 scale, or byte kb % 4 of a packed
+// UE8M0 word.
+__device__ __forceinline__ int act_e8m0(const GParams& p, uint32_t raw, int64_t kb) {
+    const int sh = p.e8 ? 8 * (int)(kb & 3) : 23;
+    return (int)((raw >> sh) & 0xFFu);
+}
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         for (int j = 0; j < 8; ++j) dma16s(ab, off[j], adst + so + j * 1024);
 #pragma unroll
         for (int j = 0; j < 8; ++j) dma16s(wb, off[8 + j], wdst + so + j * 1024);
-        dma4s(sabase + kb * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
+        dma4s(sabase + (kb >> p.kshift) * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
         dma4s(swbase + kb * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
     };
 
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
                 const v8i af = afn;
-                const int ea = e8m0_of(san);
+                const int ea = act_e8m0(p, __float_as_uint(san), kb);
                 if (mi < 7) {
                     afn = frag(sta + (mi + 1) * 2048);
                     san = sca[128 * wm + 16 * (mi + 1) + frow];
@@ -339,16 +349,19 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // the scale gather mixes two sources across lanes: 64-bit lane addresses
     const float* ssrc;
     int64_t sstep;
+    int kshl;  // K-blocks per scale word: activation words may pack four
     if (lane < 32) {
         int64_t m = m0 + 32 * (wave & 1) + lane;
         m = m < p.T ? m : p.T - 1;
         ssrc = p.sa + m * p.sst + g * p.ssg;
         sstep = p.sskb;
+        kshl = p.kshift;
     } else {
         int64_t n = n0 + 32 * (wave & 1) + (lane - 32);
         n = n < p.R ? n : p.R - 1;
         ssrc = p.sw + wscale_index(p, g * p.R + n, 0);
         sstep = 1;
+        kshl = 0;
     }
     const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
     auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
@@ -363,7 +376,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
             else
                 dma16s(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
         }
-        dma4(ssrc + kb * sstep, st + 16384 + 256 * wave);
+        dma4(ssrc + (kb >> kshl) * sstep, st + 16384 + 256 * wave);
     };
 
     if (copier) {
@@ -406,8 +419,8 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
             const uint4 hi = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
             const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             if constexpr (MX) {
-                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], e8m0_of(sc[64 * (mi >> 1) + 16 * (mi & 1) + frow]),
-                                      e8m0_of(swv));
+                const uint32_t raw = __float_as_uint(sc[64 * (mi >> 1) + 16 * (mi & 1) + frow]);
+                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], act_e8m0(p, raw, kb0 + i), e8m0_of(swv));
             } else {
                 const float4 t4 =
                     *reinterpret_cast<const float4*>(&sc[64 * (mi >> 1) + 16 * (mi & 1) + 4 * (lane >> 4)]);
@@ -477,7 +490,7 @@ void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     GParams p;
     p.a = a.a;
-    p.sa = a.sa;
+    p.sa = static_cast<const float*>(a.sa);  // fp32 scales or UE8M0 words: copied as 4-byte words
     p.w = a.w;
     p.sw = a.sw;
     p.z = a.z;
@@ -492,6 +505,8 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.ssg = a.lay.s_stride_g;
     p.sskb = a.lay.s_stride_kb;
     p.w_shift = a.w_1x128 ? 0 : 7;
+    p.e8 = a.a_e8m0;
+    p.kshift = a.a_e8m0 ? 2 : 0;
     // decode kernel for few tokens (the weight stream dominates), tile kernel otherwise
     const bool decode = a.T <= 128;
     if (decode) {

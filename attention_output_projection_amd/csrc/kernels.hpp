@@ -9,17 +9,18 @@ namespace oproj {
 
 struct ActLayout {
     int64_t stride_t, stride_g;              // codes, bytes == elements
-    int64_t s_stride_t, s_stride_g, s_stride_kb;  // scales, floats
+    int64_t s_stride_t, s_stride_g, s_stride_kb;  // scales, 4-byte words (fp32 or packed UE8M0)
 };
 
 struct RopeQuantArgs {
     int64_t T, G, hpg, max_pos;
     int pow2;
+    int e8m0;                 // write packed UE8M0 words (one per head: 4 blocks) instead of fp32
     const uint16_t* o;        // bf16 [T][G*hpg][512]
     const int64_t* positions; // [T]
     const float* cos_sin;     // [max_pos][64]
     uint8_t* codes;
-    float* scales;
+    void* scales;             // fp32 per block, or uint32 UE8M0 words
     ActLayout lay;
 };
 hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t s);
@@ -37,8 +38,9 @@ struct GroupedGemmArgs {
     int64_t T, G, D, R;
     int mx;        // both scale sets are powers of two: use block-scaled MFMA
     int w_1x128;   // weight scales per row (else 128x128 tiles of the flat matrix)
+    int a_e8m0;    // activation scales are packed UE8M0 words (implies mx)
     const uint8_t* a;
-    const float* sa;
+    const void* sa;
     ActLayout lay;
     const uint8_t* w;
     const float* sw;

@@ -19,10 +19,10 @@ struct Params {
     const int64_t* pos;
     const float* table;
     uint8_t* codes;
-    float* scales;
+    void* scales;  // fp32 per block, or packed UE8M0 words (one per head)
     int64_t T, H, hpg, max_pos, nitems;
     int64_t st, sg, sst, ssg, sskb;
-    int nchunk, pow2;
+    int nchunk, pow2, e8m0;
 };
 
 // Heads per item for a group of hpg heads: 4 (4 KiB of input per wave) when
@@ -47,7 +47,8 @@ inline Params make_params(const RopeQuantArgs& a, int ch) {
     p.sst = a.lay.s_stride_t;
     p.ssg = a.lay.s_stride_g;
     p.sskb = a.lay.s_stride_kb;
-    p.pow2 = a.pow2;
+    p.pow2 = a.pow2 | a.e8m0;
+    p.e8m0 = a.e8m0;
     return p;
 }
 
@@ -139,9 +140,21 @@ struct Wave {
         if (bad) s = __builtin_nanf("");
         const float r = 1.0f / s;
 
-        if (li < CH) {
+        if (p.e8m0) {
+            // UE8M0 byte of block (head li, block c) is the exponent field of
+            // the power-of-two scale (0xFF for NaN); lane li of row 0 packs
+            // the head's four bytes into one word, block c in byte c
+            const uint32_t e = bad ? 0xFFu : ((__float_as_uint(s) >> 23) & 0xFFu);
+            const uint32_t e1 = __shfl(e, (lane + 16) & 63), e2 = __shfl(e, (lane + 32) & 63),
+                           e3 = __shfl(e, (lane + 48) & 63);
+            if (c == 0 && li < CH) {
+                const int64_t hw = chunk * CH + li;  // head within the group = word index
+                static_cast<uint32_t*>(p.scales)[t * p.sst + g * p.ssg + hw * p.sskb] =
+                    e | (e1 << 8) | (e2 << 16) | (e3 << 24);
+            }
+        } else if (li < CH) {
             const int64_t kb = (chunk * CH + li) * 4 + c;
-            p.scales[t * p.sst + g * p.ssg + kb * p.sskb] = s;
+            static_cast<float*>(p.scales)[t * p.sst + g * p.ssg + kb * p.sskb] = s;
         }
 
         uint8_t* dst = p.codes + t * p.st + g * p.sg + chunk * CH * 512 + 8 * lane;

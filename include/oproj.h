@@ -57,8 +57,18 @@ typedef enum oproj_status {
 /* Scale recipe ([OPROJ] compute_fp8_einsum_recipe names two):
  *  OPROJ_SCALE_FP32: activation scale = amax / 448 as fp32 (1x128 blocks).
  *  OPROJ_SCALE_POW2: that value rounded up to a power of two (E8M0-style),
- *                    still stored as fp32. */
-typedef enum oproj_scale_mode { OPROJ_SCALE_FP32 = 0, OPROJ_SCALE_POW2 = 1 } oproj_scale_mode;
+ *                    still stored as fp32.
+ *  OPROJ_SCALE_E8M0: the POW2 scales stored packed ([OPROJ]
+ *                    rope_quant_attn_out: one int32 per head over its four
+ *                    128-wide blocks): byte b of activation scale word j
+ *                    (bits 8b..8b+7) is the UE8M0 byte of block 4j+b, i.e. the
+ *                    biased exponent k+127 of the scale 2^k (0xFF = NaN).
+ *                    Weight scales stay fp32 powers of two. */
+typedef enum oproj_scale_mode {
+    OPROJ_SCALE_FP32 = 0,
+    OPROJ_SCALE_POW2 = 1,
+    OPROJ_SCALE_E8M0 = 2
+} oproj_scale_mode;
 
 /* Weight scale blocks:
  *  OPROJ_WBLOCK_128x128: scale (i, kb) covers rows 128i..128i+127 of the flat
@@ -90,6 +100,9 @@ typedef struct oproj_shape {
  *                     [FUSED] returns ([T,G,D] viewed with strides (D, T*D, 1))
  *  scales [G][KB][T]  (s_stride_t = 1, s_stride_kb = T, s_stride_g = KB*T),
  *                     i.e. MN-major, tokens contiguous.
+ * In OPROJ_SCALE_E8M0 mode a scale is a 4-byte word holding four blocks and
+ * kb above counts words (kb < KB/4); the default is then [G][KB/4][T]
+ * (s_stride_t = 1, s_stride_kb = T, s_stride_g = (KB/4)*T).
  * stride_t and stride_g must be multiples of 16. */
 typedef struct oproj_act_layout {
     int64_t stride_t, stride_g;
@@ -108,11 +121,12 @@ typedef struct oproj_act_layout {
  *  positions  int64 [T]
  *  cos_sin    fp32 [max_pos][64]: cos[0..31] then sin[0..31]
  *  a_codes    FP8 codes, layout `out_layout` (NULL: default group-major)
- *  a_scales   fp32 scales, layout `out_layout`
+ *  a_scales   fp32 scales (uint32 UE8M0 words in OPROJ_SCALE_E8M0 mode),
+ *             layout `out_layout`
  * Codes and scales of groups the layout does not name are untouched. */
 oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
                                   const int64_t* positions, const float* cos_sin, void* a_codes,
-                                  float* a_scales, const oproj_act_layout* out_layout,
+                                  void* a_scales, const oproj_act_layout* out_layout,
                                   void* stream);
 
 /* Step a3 ([OPROJ] deep_gemm_fp8_o_proj's einsum "bhr,hdr->bhd"; [GWA]):
@@ -128,11 +142,12 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
  *  w_scales  fp32, blocks per `w_block`
  *  scale_mode  OPROJ_SCALE_POW2 declares that BOTH activation and weight
  *              scales are powers of two (they are then applied by the matrix
- *              cores' block scaling); OPROJ_SCALE_FP32 accepts any positive
- *              fp32 scales.
+ *              cores' block scaling); OPROJ_SCALE_E8M0 is the same with the
+ *              activation scales as packed UE8M0 words; OPROJ_SCALE_FP32
+ *              accepts any positive fp32 scales.
  *  z         bf16 [T][G][R] contiguous */
 oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
-                                const float* a_scales, const oproj_act_layout* a_layout,
+                                const void* a_scales, const oproj_act_layout* a_layout,
                                 const void* w_codes, const float* w_scales, int32_t w_block,
                                 void* z, void* stream);
 
@@ -201,7 +216,8 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
 /* Offline weight preparation ([OPROJ] compute_fp8_einsum_recipe; [SGL]
  * _setup_fp8_wo_a_scales): quantise fp32 w[rows][K] to FP8 codes with one
  * scale per block (128x128 or 1x128 per `w_block`), scale = amax/448
- * (pow2: rounded up to a power of two), code = e4m3fn(w / scale).
+ * (pow2: rounded up to a power of two; OPROJ_SCALE_E8M0 gives the same fp32
+ * powers of two), code = e4m3fn(w / scale).
  *  w        fp32 [rows][K];  codes FP8 [rows][K];  scales fp32 (see oproj_wblock)
  *  K must be a multiple of 128. */
 oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,

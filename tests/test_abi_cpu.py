@@ -177,7 +177,7 @@ def test_quantize_weight_validation(lib):
     assert f(0, 128) == E_OK
     assert f(4, 100) == E_SHAPE
     assert f(4, 128, blk=2) == E_MODE
-    assert f(4, 128, mode=2) == E_MODE
+    assert f(4, 128, mode=3) == E_MODE
     assert f(4, 128, w=None) == E_NULL
     assert f(4, 128, s=0x1002) == E_ALIGN
 

@@ -480,3 +480,99 @@ def test_full_path_with_wo_b_sampled():
     got = yg[toks[idx[:, 0]], idx[:, 1]]
     e = U.rel_max_err(got, ref)
     assert e <= TOL, e
+
+
+# ---------------------------------------------------------------- packed UE8M0 activation scales
+def _quant_both_modes(w, o, pos, tab):
+    """GPU a1+a2 in POW2 mode (fp32 scales) and in E8M0 mode (packed words), default layouts."""
+    T = o.shape[0]
+    shp = _shape(w, T)
+    d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
+    c2 = torch.empty((w.n_groups, T, w.D), dtype=torch.uint8, device=DEV)
+    s2 = torch.empty((w.n_groups, w.KB, T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, ap.OPROJ_SCALE_POW2, d_o, d_pos, d_tab, c2, s2)
+    c8 = torch.empty_like(c2)
+    s8 = torch.empty((w.n_groups, w.KB // 4, T), dtype=torch.int32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, ap.OPROJ_SCALE_E8M0, d_o, d_pos, d_tab, c8, s8)
+    return c2, s2, c8, s8
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "full"])
+def test_inv_rope_quant_e8m0_words(name):
+    """E8M0 mode: codes equal the POW2 mode's; the packed words are bit-exact
+    against the oracle's packing of its pow2 scales."""
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    c2, s2, c8, s8 = _quant_both_modes(w, o, pos, tab)
+    assert torch.equal(c2, c8)
+    _, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=True)
+    want = oracle.e8m0_pack(sr)  # [T, G, KB/4]
+    got = np.ascontiguousarray(np.transpose(_host(s8).view(np.uint32), (2, 0, 1)))
+    assert np.array_equal(got, want)
+
+
+def test_inv_rope_quant_e8m0_bad_position_is_ff():
+    w = wl.WORKLOADS["tiny"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w).copy(), wl.table(w)
+    pos[2] = -1
+    _, _, _, s8 = _quant_both_modes(w, o, pos, tab)
+    b = _host(s8).view(np.uint8).reshape(w.n_groups, w.KB // 4, w.T, 4)
+    assert (b[:, :, 2, :] == 0xFF).all() and (b[:, :, [0, 1, 3], :] != 0xFF).all()
+
+
+@pytest.mark.parametrize("T", [64, 300])
+def test_grouped_gemm_e8m0_equals_pow2(T):
+    """The GEMM fed packed UE8M0 words gives the same z, bit for bit, as with
+    the fp32 powers of two (few-token and tile kernels), and meets the bar."""
+    w = wl.WORKLOADS["decode"].scaled(T)
+    o, tab = wl.attn_out(w), wl.table(w)
+    pos = wl.uniform_int(wl.seed_of(77, T), T, 0, w.max_pos)
+    c2, s2, c8, s8 = _quant_both_modes(w, o, pos, tab)
+    wmat = wl.wo_a_f32(w)
+    d_wq, d_ws = gpu_weight(wmat, 1, True)
+    shp = _shape(w, T)
+    z2 = torch.empty((T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    z8 = torch.empty_like(z2)
+    ap.oproj_grouped_wo_a(shp, ap.OPROJ_SCALE_POW2, c2, s2, None, d_wq, d_ws, ap.OPROJ_WBLOCK_1x128, z2)
+    ap.oproj_grouped_wo_a(shp, ap.OPROJ_SCALE_E8M0, c8, s8, None, d_wq, d_ws, ap.OPROJ_WBLOCK_1x128, z8)
+    assert torch.equal(z2, z8)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=True)
+    qw, sw = oracle.quant_weight(wmat, 1, True)
+    rng = np.random.default_rng(78)
+    idx = U.sample_triples(rng, T, w.n_groups, w.o_lora_rank, 2000)
+    ref = oracle.grouped_gemm(qr, sr, qw, sw, w.n_groups, w.o_lora_rank, 1, idx=idx)
+    zg = U.bf16_bits_to_f64(_host(z8).view(np.uint16))
+    assert U.rel_max_err(zg[idx[:, 0], idx[:, 1], idx[:, 2]], ref) <= TOL
+
+
+def test_grouped_gemm_e8m0_token_major_layout():
+    """Packed words in a token-major [T][G][KB/4] layout through the strides."""
+    w = wl.WORKLOADS["tiny"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=True)
+    words = oracle.e8m0_pack(sr)  # [T, G, KB/4]
+    wmat = wl.wo_a_f32(w)
+    d_wq, d_ws = gpu_weight(wmat, 128, True)
+    lay = ap.ActLayout(w.n_groups * w.D, w.D, w.n_groups * (w.KB // 4), w.KB // 4, 1)
+    z = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    ap.oproj_grouped_wo_a(_shape(w), ap.OPROJ_SCALE_E8M0, _dev(qr), _dev(words.view(np.int32)), lay,
+                          d_wq, d_ws, ap.OPROJ_WBLOCK_128x128, z)
+    qw, sw = oracle.quant_weight(wmat, 128, True)
+    ref = oracle.grouped_gemm(qr, sr, qw, sw, w.n_groups, w.o_lora_rank, 128)
+    assert U.rel_max_err(U.bf16_bits_to_f64(_host(z).view(np.uint16)), ref) <= TOL
+
+
+def test_fused_e8m0_equals_steps():
+    w = wl.WORKLOADS["decode"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws = gpu_weight(wl.wo_a_f32(w), 128, True)
+    shp = _shape(w)
+    d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    zf = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    ap.oproj_fused(shp, ap.OPROJ_SCALE_E8M0, d_o, d_pos, d_tab, d_wq, d_ws, 0, None, 0, ws, nbytes, zf)
+    _, _, c8, s8 = _quant_both_modes(w, o, pos, tab)
+    zs = torch.empty_like(zf)
+    ap.oproj_grouped_wo_a(shp, ap.OPROJ_SCALE_E8M0, c8, s8, None, d_wq, d_ws, 0, zs)
+    assert torch.equal(zf, zs)
