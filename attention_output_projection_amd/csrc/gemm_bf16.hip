@@ -191,13 +191,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
 // ---------------------------------------------------------------------------
 // Few-token kernel (M <= 128): the weight stream is the cost, so the tile is
 // 64 rows x 64 columns (no rows computed for nothing) and, as in the FP8
-// decode kernel, the eight waves form two K-groups of four that each walk
-// half of K through their own ring of XNS steps (XNS-1 in flight), one
-// 64-element step (128 bytes of every row) per s_waitcnt + barrier.  In a
-// K-group waves 0-1 copy (weights with the non-temporal hint: read once)
-// and all four compute, wave w owning columns 16w..16w+15.  The K-groups'
-// fp32 partial tiles are summed through LDS and stored as whole rows.
-constexpr int XBM = 64, XBN = 64, XNS = 4, XKS = 2;
+// decode kernel, the waves form K-groups of four that each walk their share
+// of K through their own ring of XNS steps (XNS-1 in flight), one 64-element
+// step (128 bytes of every row) per s_waitcnt + barrier.  Four K-groups with
+// two-slot rings measured faster than two with four slots: more positions
+// along K in flight at once.  In a K-group waves 0-1 copy (weights with the
+// non-temporal hint: read once) and all four compute, wave w owning columns
+// 16w..16w+15.  The K-groups' fp32 partial tiles are summed through LDS and
+// stored as whole rows.
+#ifndef OPROJ_XNS
+#define OPROJ_XNS 2
+#endif
+#ifndef OPROJ_XKS
+#define OPROJ_XKS 4
+#endif
+constexpr int XBM = 64, XBN = 64, XNS = OPROJ_XNS, XKS = OPROJ_XKS;
 constexpr int XSTAGE = 64 * 128 * 2;  // activation slab + weight slab
 constexpr int XVM = 8;                // copy instructions per copying wave per step
 constexpr int XPROW = XBN + 4;        // fp32 per row of an epilogue partial tile

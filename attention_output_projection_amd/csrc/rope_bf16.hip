@@ -9,12 +9,13 @@
 // x(t, g, (h % hpg)*512 + k) = o(t, h, k) for k < 448; the 64 RoPE dims of
 // each head are rotated by -theta with the same fp32 operation order as the
 // quantising kernel (e' = fma(d, s, e*c), d' = fma(-e, s, d*c)) and rounded
-// to bf16, nearest even.  Work unit: one wave per four consecutive head rows;
+// to bf16, nearest even.  Work unit: one wave per two consecutive head rows;
 // lane l moves elements 8l..8l+7 of each (16-byte non-temporal loads and
 // stores), lanes 56..63 hold the RoPE dims and fetch cos[4(l-56)..+3],
 // sin[..] of each row's token position.  Items are numbered in address order
-// and dealt round-robin over a fixed population of waves, each of which loads
-// its next item while it stores the current one.  HBM-bound: 1 KiB read + 1 KiB
+// and dealt round-robin over a fixed population of waves (32 per CU, the
+// occupancy limit: measured best), each of which loads its next item while
+// it stores the current one.  HBM-bound: 1 KiB read + 1 KiB
 // written per head row.  A position outside [0, max_pos) writes NaN into the
 // token's RoPE dims.
 #include "device_common.hpp"
@@ -38,7 +39,10 @@ struct RBParams {
     int64_t H, hpg, max_pos, nrows, nitems, st, sg;
 };
 
-constexpr int kRbRows = 4;  // head rows per work item (4 KiB read per wave in flight)
+#ifndef OPROJ_RB_ROWS
+#define OPROJ_RB_ROWS 2
+#endif
+constexpr int kRbRows = OPROJ_RB_ROWS;  // head rows per work item
 
 struct RbItem {
     rb_u32x4 raw[kRbRows];
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kRbWaves * 64) void inv_rope_bf16_kernel(RBParams p
 }  // namespace
 
 #ifndef OPROJ_RB_WAVES_PER_CU
-#define OPROJ_RB_WAVES_PER_CU 16
+#define OPROJ_RB_WAVES_PER_CU 32
 #endif
 
 hipError_t launch_inv_rope_bf16(const RopeBf16Args& a, hipStream_t stream) {
