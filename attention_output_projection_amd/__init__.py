@@ -24,6 +24,8 @@ from ._native import (  # noqa: F401
     load_library,
     oproj_dense_bf16_gemm,
     oproj_fused,
+    oproj_fused_bf16,
+    oproj_fused_bf16_workspace_bytes,
     oproj_fused_workspace_bytes,
     oproj_grouped_wo_a,
     oproj_grouped_wo_a_bf16,

@@ -120,6 +120,8 @@ def load_library():
             "oproj_grouped_wo_a_bf16": (I32, [SP, P, BP, P, P, P]),
             "oproj_dense_bf16_gemm": (I32, [I64, I64, I64, P, P, P, P]),
             "oproj_fused_workspace_bytes": (SZ, [SP, I64]),
+            "oproj_fused_bf16_workspace_bytes": (SZ, [SP, I64]),
+            "oproj_fused_bf16": (I32, [SP, P, P, P, P, P, I64, P, SZ, P, P]),
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
             "oproj_quantize_weight": (I32, [I64, I64, I32, I32, P, P, P, P]),
             "oproj_status_string": (ctypes.c_char_p, [I32]),
@@ -217,6 +219,18 @@ def oproj_fused(shape: Shape, scale_mode: int, o, positions, cos_sin, w_codes, w
         _ptr(w_scales), w_block, _ptr(wo_b), hidden, _ptr(workspace), workspace_bytes, _ptr(out),
         _stream(stream))
     _check("oproj_fused", st)
+
+
+def oproj_fused_bf16_workspace_bytes(shape: Shape, hidden: int = 0) -> int:
+    return int(load_library().oproj_fused_bf16_workspace_bytes(ctypes.byref(shape._c()), hidden))
+
+
+def oproj_fused_bf16(shape: Shape, o, positions, cos_sin, w, wo_b, hidden: int, workspace,
+                     workspace_bytes: int, out, stream=None) -> None:
+    st = load_library().oproj_fused_bf16(
+        ctypes.byref(shape._c()), _ptr(o), _ptr(positions), _ptr(cos_sin), _ptr(w), _ptr(wo_b), hidden,
+        _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream))
+    _check("oproj_fused_bf16", st)
 
 
 def oproj_quantize_weight(rows: int, K: int, w_block: int, scale_mode: int, w, codes, scales,

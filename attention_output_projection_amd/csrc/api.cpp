@@ -276,6 +276,45 @@ oproj_status oproj_grouped_wo_a_bf16(const oproj_shape* shape, const void* x,
     return from_hip(oproj::launch_bf16_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t oproj_fused_bf16_workspace_bytes(const oproj_shape* shape, int64_t hidden) {
+    if (check_shape(shape, true) != OPROJ_OK) return 0;
+    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;
+    const size_t D = (size_t)shape->heads_per_group * 512;
+    size_t b = round_up(T * G * D * 2);
+    if (hidden > 0) b += round_up(T * G * (size_t)shape->o_lora_rank * 2);
+    return b;
+}
+
+oproj_status oproj_fused_bf16(const oproj_shape* shape, const void* o, const int64_t* positions,
+                              const float* cos_sin, const void* w, const void* wo_b, int64_t hidden,
+                              void* workspace, size_t workspace_bytes, void* out, void* stream) {
+    oproj_status st = check_shape(shape, true);
+    if (st != OPROJ_OK) return st;
+    if (wo_b && (hidden < 16 || hidden % 16 != 0)) return OPROJ_E_SHAPE;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!o || !positions || !cos_sin || !w || !workspace || !out) return OPROJ_E_NULL;
+    if (workspace_bytes < oproj_fused_bf16_workspace_bytes(shape, wo_b ? hidden : 0)) return OPROJ_E_SHAPE;
+    if (!aligned16(workspace) || !aligned16(o) || !aligned16(cos_sin) || !aligned16(w) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(positions) & 7u))
+        return OPROJ_E_ALIGN;
+    const int64_t T = shape->T, G = shape->n_groups, R = shape->o_lora_rank;
+    const int64_t D = shape->heads_per_group * 512, lim = int64_t(1) << 32;
+    // the GEMM kernels address each group's operands as a base plus 32-bit lane offsets
+    if ((T - 1) * G * D * 2 + D * 2 > lim || R * D * 2 > lim) return OPROJ_E_SHAPE;
+    if (wo_b) {
+        const int64_t K = G * R;
+        if (K % 64 != 0 || T * K * 2 > lim || hidden * K * 2 > lim) return OPROJ_E_SHAPE;
+        if (!aligned16(wo_b)) return OPROJ_E_ALIGN;
+    }
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* x = ws;
+    void* zbuf = wo_b ? (void*)(ws + round_up((size_t)(T * G * D * 2))) : out;
+    if ((st = oproj_inv_rope_bf16(shape, o, positions, cos_sin, x, nullptr, stream)) != OPROJ_OK) return st;
+    if ((st = oproj_grouped_wo_a_bf16(shape, x, nullptr, w, zbuf, stream)) != OPROJ_OK) return st;
+    if (!wo_b) return OPROJ_OK;
+    return oproj_dense_bf16_gemm(T, hidden, G * R, zbuf, wo_b, out, stream);
+}
+
 size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden) {
     if (check_shape(shape, true) != OPROJ_OK) return 0;
     const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;

@@ -197,6 +197,20 @@ oproj_status oproj_grouped_wo_a_bf16(const oproj_shape* shape, const void* x,
                                      const oproj_bf16_layout* x_layout, const void* w, void* z,
                                      void* stream);
 
+/* Bytes of caller-provided workspace oproj_fused_bf16 needs: the bf16 x and,
+ * when hidden > 0, the bf16 z; each region 256-byte aligned. */
+size_t oproj_fused_bf16_workspace_bytes(const oproj_shape* shape, int64_t hidden);
+
+/* The unquantised path in one call ([OPROJ] deep_gemm_fp8_o_proj without
+ * FP8): the bf16 rotation into the workspace (token-major x), the grouped
+ * bf16 GEMM, and when wo_b != NULL the dense GEMM over z.flatten(1).
+ *  w    bf16 [G*R][D];  wo_b bf16 [hidden][G*R] or NULL
+ *  out  z bf16 [T][G][R] when wo_b == NULL, else y bf16 [T][hidden]
+ * Every argument is validated before the first launch. */
+oproj_status oproj_fused_bf16(const oproj_shape* shape, const void* o, const int64_t* positions,
+                              const float* cos_sin, const void* w, const void* wo_b, int64_t hidden,
+                              void* workspace, size_t workspace_bytes, void* out, void* stream);
+
 /* Bytes of caller-provided workspace oproj_fused needs: the FP8 codes, the
  * scales and, when hidden > 0, the bf16 z; each region 256-byte aligned. */
 size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden);

@@ -149,6 +149,23 @@ def test_grouped_wo_a_bf16_validation(lib):
     assert _gb(_shape(T=1 << 20), layout=_native.Bf16Layout(4096, 1024)) == E_SHAPE
 
 
+def test_fused_bf16_workspace_and_validation(lib):
+    shp = _shape(T=4, n_groups=2, heads_per_group=2, o_lora_rank=64)
+    D = 2 * 512
+    want = (4 * 2 * D * 2 + 255) // 256 * 256
+    assert ap.oproj_fused_bf16_workspace_bytes(shp, 0) == want
+    assert ap.oproj_fused_bf16_workspace_bytes(shp, 32) == want + (4 * 2 * 64 * 2 + 255) // 256 * 256
+    f = lambda shape, ws_bytes=1 << 20, wo_b=None, hidden=0, o=0x1000, out=0x1000, ws=0x1000: _raw(
+        "oproj_fused_bf16", ctypes.byref(shape._c()), o, 0x1000, 0x1000, 0x1000, wo_b, hidden, ws, ws_bytes,
+        out, None)
+    assert f(_shape(T=0), o=None, out=None, ws=None) == E_OK
+    assert f(shp, o=None) == E_NULL
+    assert f(shp, ws_bytes=16) == E_SHAPE
+    assert f(shp, ws=BAD) == E_ALIGN
+    assert f(shp, wo_b=0x1000, hidden=10) == E_SHAPE
+    assert f(shp, wo_b=BAD, hidden=32) == E_ALIGN
+
+
 def test_fused_workspace_and_validation(lib):
     shp = _shape(T=64, n_groups=16, heads_per_group=8, o_lora_rank=1024, max_pos=32768)
     n0 = ap.oproj_fused_workspace_bytes(shp, 0)

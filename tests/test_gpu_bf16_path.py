@@ -163,3 +163,37 @@ def test_grouped_wo_a_bf16_group_isolation():
     wq2[64:128] = wl.f32_to_bf16_bits(np.full((64, w.D), 0.5, np.float32))
     z2 = gpu_gemm_bf16(w, x, wq2)
     assert np.array_equal(z2[:, [0, 2]], z[:, [0, 2]]) and not np.array_equal(z2[:, 1], z[:, 1])
+
+
+@pytest.mark.parametrize("name,with_wo_b", [("decode", False), ("tiny", False), ("decode", True)])
+def test_fused_bf16_equals_steps(name, with_wo_b):
+    """oproj_fused_bf16 equals the separate calls bit for bit; with wo_b the
+    result also meets the bar against the oracle chain."""
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    wq = wl.wo_a_bf16(w)
+    shp = _shape(w)
+    hidden = 512 if with_wo_b else 0
+    wob = wl.bf16_matrix(wl.seed_of(w.wid, 12), hidden, w.n_groups * w.o_lora_rank, 0.02) if with_wo_b else None
+    d_o, d_pos, d_tab, d_w = _dev(o.view(np.int16)), _dev(pos), _dev(tab), _dev(wq.view(np.int16))
+    d_wob = _dev(wob.view(np.int16)) if with_wo_b else None
+    nbytes = ap.oproj_fused_bf16_workspace_bytes(shp, hidden)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.T, hidden) if with_wo_b else (w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16,
+                      device=DEV)
+    ap.oproj_fused_bf16(shp, d_o, d_pos, d_tab, d_w, d_wob, hidden, ws, nbytes, out)
+    x = torch.empty((w.T, w.n_groups, w.D), dtype=torch.int16, device=DEV)
+    z = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    ap.oproj_inv_rope_bf16(shp, d_o, d_pos, d_tab, x)
+    ap.oproj_grouped_wo_a_bf16(shp, x, None, d_w, z)
+    if not with_wo_b:
+        assert torch.equal(out, z)
+        return
+    y = torch.empty_like(out)
+    ap.oproj_dense_bf16_gemm(w.T, hidden, w.n_groups * w.o_lora_rank, z, d_wob, y)
+    assert torch.equal(out, y)
+    xr = oracle.inv_rope_bf16(o, pos, tab).reshape(w.T, w.n_groups, w.D)
+    zr = oracle.f64_to_bf16(oracle.grouped_gemm_bf16(xr, wq, w.n_groups, w.o_lora_rank))
+    yr = oracle.dense_gemm_bf16(zr.reshape(w.T, -1), wob)
+    e = U.rel_max_err(U.bf16_bits_to_f64(_host(out).view(np.uint16)), yr)
+    assert e <= TOL, e
