@@ -27,7 +27,8 @@
 // non-temporal loads and stores (each byte is touched once here).  The
 // kernel is HBM-bound: read 1 KiB + write 512 B per head row; a moderate
 // population of waves (12 per CU) keeps enough in flight without crowding
-// the memory controllers.
+// the memory controllers.  Small batches (a few thousand head rows) are
+// latency-bound instead: items of two heads, one wave each.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "rq_item.hpp"
@@ -131,12 +132,17 @@ __global__ __launch_bounds__(kWqThreads) void quantize_weight_kernel(const float
 #endif
 
 hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
-    const int ch = rq::heads_per_item(a.hpg);  // 1, 2 or 4
+    int ch = rq::heads_per_item(a.hpg);  // 1, 2 or 4
+    // small batches: two-head items when that still gives every item its own
+    // wave within the occupancy limit (32 waves per CU) -- the kernel is then
+    // latency-bound and more, smaller items finish sooner (measured)
+    const bool small = ch == 4 && a.T * a.G * (a.hpg / 2) <= 256 * 32;
+    if (small) ch = 2;
     const RQParams p = rq::make_params(a, ch);
-    // a fixed population of waves (OPROJ_Q_WAVES_PER_CU per CU on 256 CUs)
-    // walks the items; small batches get one wave per item
+    // otherwise a fixed population of waves (OPROJ_Q_WAVES_PER_CU per CU on
+    // 256 CUs) walks the items
     int64_t waves = 256 * OPROJ_Q_WAVES_PER_CU;
-    if (p.nitems < waves) waves = p.nitems;
+    if (small || p.nitems < waves) waves = p.nitems;
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kWaves * 64);
     const bool pipe = p.nitems > waves;  // else every wave takes exactly one item
