@@ -14,6 +14,7 @@ from ._native import (  # noqa: F401
     OPROJ_SCALE_FP32,
     OPROJ_SCALE_POW2,
     OPROJ_WBLOCK_1x128,
+    OPROJ_WBLOCK_1x128_UE8M0,
     OPROJ_WBLOCK_128x128,
     ActLayout,
     Bf16Layout,

@@ -15,6 +15,7 @@ OPROJ_SCALE_POW2 = 1
 OPROJ_SCALE_E8M0 = 2
 OPROJ_WBLOCK_128x128 = 0
 OPROJ_WBLOCK_1x128 = 1
+OPROJ_WBLOCK_1x128_UE8M0 = 2
 
 _STATUS = {0: "OPROJ_OK", 1: "OPROJ_E_NULL", 2: "OPROJ_E_SHAPE", 3: "OPROJ_E_ALIGN",
            4: "OPROJ_E_MODE", 5: "OPROJ_E_HIP"}

@@ -37,6 +37,12 @@ bool valid_mode(int32_t m) {
     return m == OPROJ_SCALE_FP32 || m == OPROJ_SCALE_POW2 || m == OPROJ_SCALE_E8M0;
 }
 
+// weight block mode valid with this scale mode (UE8M0 words need power-of-two scales)
+bool valid_wblock(int32_t b, int32_t mode) {
+    if (b == OPROJ_WBLOCK_128x128 || b == OPROJ_WBLOCK_1x128) return true;
+    return b == OPROJ_WBLOCK_1x128_UE8M0 && mode != OPROJ_SCALE_FP32;
+}
+
 // default layout; in UE8M0 mode a scale word covers four K-blocks
 oproj::ActLayout default_layout(const oproj_shape* s, int32_t mode) {
     const int64_t D = s->heads_per_group * 512, KB = D / 128 / (mode == OPROJ_SCALE_E8M0 ? 4 : 1);
@@ -123,12 +129,12 @@ oproj_status prep_quant(const oproj_shape* shape, int32_t scale_mode, const void
 
 // Validation + argument set-up of step a3 (shared by the entry points).
 oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void* a_codes, const void* a_scales,
-                       const oproj_act_layout* a_layout, const void* w_codes, const float* w_scales,
+                       const oproj_act_layout* a_layout, const void* w_codes, const void* w_scales,
                        int32_t w_block, void* z, oproj::GroupedGemmArgs* a) {
     oproj_status st = check_shape(shape, true);
     if (st != OPROJ_OK) return st;
     if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
-    if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
+    if (!valid_wblock(w_block, scale_mode)) return OPROJ_E_MODE;
     if ((st = check_layout(a_layout)) != OPROJ_OK) return st;
     if (shape->T == 0) return OPROJ_OK;
     if (!a_codes || !a_scales || !w_codes || !w_scales || !z) return OPROJ_E_NULL;
@@ -150,7 +156,8 @@ oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void*
     a->R = shape->o_lora_rank;
     a->mx = scale_mode != OPROJ_SCALE_FP32;
     a->a_e8m0 = scale_mode == OPROJ_SCALE_E8M0;
-    a->w_1x128 = w_block == OPROJ_WBLOCK_1x128;
+    a->w_1x128 = w_block != OPROJ_WBLOCK_128x128;
+    a->w_e8m0 = w_block == OPROJ_WBLOCK_1x128_UE8M0;
     a->a = static_cast<const uint8_t*>(a_codes);
     a->sa = a_scales;
     a->lay = to_layout(a_layout, shape, scale_mode);
@@ -174,7 +181,7 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
 
 oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
                                 const void* a_scales, const oproj_act_layout* a_layout,
-                                const void* w_codes, const float* w_scales, int32_t w_block,
+                                const void* w_codes, const void* w_scales, int32_t w_block,
                                 void* z, void* stream) {
     oproj::GroupedGemmArgs a;
     const oproj_status st =
@@ -326,12 +333,12 @@ size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden) {
 
 oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const void* o,
                          const int64_t* positions, const float* cos_sin, const void* w_codes,
-                         const float* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
+                         const void* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
                          void* workspace, size_t workspace_bytes, void* out, void* stream) {
     oproj_status st = check_shape(shape, true);
     if (st != OPROJ_OK) return st;
     if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
-    if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
+    if (!valid_wblock(w_block, scale_mode)) return OPROJ_E_MODE;
     if (wo_b && (hidden < 16 || hidden % 16 != 0)) return OPROJ_E_SHAPE;
     if (shape->T == 0) return OPROJ_OK;
     if (!o || !positions || !cos_sin || !w_codes || !w_scales || !workspace || !out)
@@ -365,10 +372,10 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
 }
 
 oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
-                                   const float* w, void* codes, float* scales, void* stream) {
+                                   const float* w, void* codes, void* scales, void* stream) {
     if (rows < 0 || K < 128 || K % 128 != 0) return OPROJ_E_SHAPE;
-    if (w_block != OPROJ_WBLOCK_128x128 && w_block != OPROJ_WBLOCK_1x128) return OPROJ_E_MODE;
-    if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
+    if (!valid_mode(scale_mode) || !valid_wblock(w_block, scale_mode)) return OPROJ_E_MODE;
+    if (w_block == OPROJ_WBLOCK_1x128_UE8M0 && K % 512 != 0) return OPROJ_E_SHAPE;
     if (rows == 0) return OPROJ_OK;
     if (!w || !codes || !scales) return OPROJ_E_NULL;
     if ((reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
@@ -376,7 +383,8 @@ oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int
     oproj::WeightQuantArgs a;
     a.rows = rows;
     a.K = K;
-    a.brows = w_block == OPROJ_WBLOCK_1x128 ? 1 : 128;
+    a.brows = w_block == OPROJ_WBLOCK_128x128 ? 128 : 1;
+    a.e8m0 = w_block == OPROJ_WBLOCK_1x128_UE8M0;
     a.pow2 = scale_mode != OPROJ_SCALE_FP32;  // weight scales stay fp32 powers of two in UE8M0 mode
     a.w = w;
     a.codes = static_cast<uint8_t*>(codes);

@@ -56,6 +56,9 @@ struct GParams {
     int64_t st, sg, sst, ssg, sskb;
     int64_t mtiles, ntiles;
     int w_shift;  // 7: 128x128 weight scales; 0: per row
+    int64_t kbw;  // weight scale words per scale row (KB, or KB/4 for packed UE8M0)
+    int wkshift;  // weight scale words hold 1 << wkshift K-blocks (0: fp32, 2: packed UE8M0)
+    int we8;      // weight scales are packed UE8M0 words (block scaled MFMA only)
     int kshift;   // activation scale words hold 1 << kshift K-blocks (0: fp32, 2: packed UE8M0)
     int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
 };
@@ -85,7 +88,13 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
 }
 
 __device__ __forceinline__ int64_t wscale_index(const GParams& p, int64_t wrow, int64_t kb) {
-    return (wrow >> p.w_shift) * p.KB + kb;
+    return (wrow >> p.w_shift) * p.kbw + (kb >> p.wkshift);
+}
+
+// Exponent byte (E8M0) of weight scale word `raw` for K-block kb (as act_e8m0).
+__device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb) {
+    const int sh = p.we8 ? 8 * (int)(kb & 3) : 23;
+    return (int)((raw >> sh) & 0xFFu);
 }
 
 // ---------------------------------------------------------------------------
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) dma16s(wb, off[8 + j], wdst + so + j * 1024);
         dma4s(sabase + (kb >> p.kshift) * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
-        dma4s(swbase + kb * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
+        dma4s(swbase + (kb >> p.wkshift) * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
     };
 
     if (copier) issue(0, 0);
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         if constexpr (MX) {
             int eb[4];
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) eb[ni] = e8m0_of(scw[64 * wn + 16 * ni + frow]);
+            for (int ni = 0; ni < 4; ++ni) eb[ni] = w_e8m0(p, __float_as_uint(scw[64 * wn + 16 * ni + frow]), kb);
             float san = sca[128 * wm + frow];
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
@@ -361,7 +370,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         n = n < p.R ? n : p.R - 1;
         ssrc = p.sw + wscale_index(p, g * p.R + n, 0);
         sstep = 1;
-        kshl = 0;
+        kshl = p.wkshift;
     }
     const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
     auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
@@ -420,7 +429,8 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
             const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             if constexpr (MX) {
                 const uint32_t raw = __float_as_uint(sc[64 * (mi >> 1) + 16 * (mi & 1) + frow]);
-                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], act_e8m0(p, raw, kb0 + i), e8m0_of(swv));
+                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], act_e8m0(p, raw, kb0 + i),
+                                      w_e8m0(p, __float_as_uint(swv), kb0 + i));
             } else {
                 const float4 t4 =
                     *reinterpret_cast<const float4*>(&sc[64 * (mi >> 1) + 16 * (mi & 1) + 4 * (lane >> 4)]);
@@ -492,7 +502,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.a = a.a;
     p.sa = static_cast<const float*>(a.sa);  // fp32 scales or UE8M0 words: copied as 4-byte words
     p.w = a.w;
-    p.sw = a.sw;
+    p.sw = static_cast<const float*>(a.sw);  // fp32 scales or UE8M0 words: copied as 4-byte words
     p.z = a.z;
     p.T = a.T;
     p.G = a.G;
@@ -505,6 +515,9 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.ssg = a.lay.s_stride_g;
     p.sskb = a.lay.s_stride_kb;
     p.w_shift = a.w_1x128 ? 0 : 7;
+    p.we8 = a.w_e8m0;
+    p.wkshift = a.w_e8m0 ? 2 : 0;
+    p.kbw = a.w_e8m0 ? p.KB / 4 : p.KB;
     p.e8 = a.a_e8m0;
     p.kshift = a.a_e8m0 ? 2 : 0;
     // decode kernel for few tokens (the weight stream dominates), tile kernel otherwise

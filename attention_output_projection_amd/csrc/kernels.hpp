@@ -28,9 +28,10 @@ hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t s);
 struct WeightQuantArgs {
     int64_t rows, K, brows;
     int pow2;
+    int e8m0;  // write UE8M0 bytes (packed four per word along K) instead of fp32
     const float* w;
     uint8_t* codes;
-    float* scales;
+    void* scales;
 };
 hipError_t launch_quantize_weight(const WeightQuantArgs& a, hipStream_t s);
 
@@ -39,11 +40,12 @@ struct GroupedGemmArgs {
     int mx;        // both scale sets are powers of two: use block-scaled MFMA
     int w_1x128;   // weight scales per row (else 128x128 tiles of the flat matrix)
     int a_e8m0;    // activation scales are packed UE8M0 words (implies mx)
+    int w_e8m0;    // weight scales are packed UE8M0 words, per row (implies mx and w_1x128)
     const uint8_t* a;
     const void* sa;
     ActLayout lay;
     const uint8_t* w;
-    const float* sw;
+    const void* sw;  // fp32 scales or packed UE8M0 words
     uint16_t* z;   // bf16 [T][G][R]
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t s);

@@ -93,9 +93,9 @@ constexpr int kWqThreads = 256;
 
 __global__ __launch_bounds__(kWqThreads) void quantize_weight_kernel(const float* __restrict__ w,
                                                                     uint8_t* __restrict__ codes,
-                                                                    float* __restrict__ scales,
+                                                                    void* __restrict__ scales,
                                                                     int64_t rows, int64_t K,
-                                                                    int64_t brows, int pow2) {
+                                                                    int64_t brows, int pow2, int e8m0) {
     __shared__ float red[kWqThreads / 64];
     const int64_t rb = blockIdx.x;
     const int64_t kb = blockIdx.y;
@@ -117,7 +117,12 @@ __global__ __launch_bounds__(kWqThreads) void quantize_weight_kernel(const float
     float s = fmaxf(a, kAmaxFloor) / kFp8Max;
     if (pow2) s = pow2_ceil(s);
     const float r = 1.0f / s;
-    if (threadIdx.x == 0) scales[rb * (K / 128) + kb] = s;
+    if (threadIdx.x == 0) {
+        if (e8m0)  // byte kb of the row: byte kb % 4 of word kb / 4, words in memory order
+            static_cast<uint8_t*>(scales)[rb * (K / 128) + kb] = (uint8_t)((__float_as_uint(s) >> 23) & 0xFFu);
+        else
+            static_cast<float*>(scales)[rb * (K / 128) + kb] = s;
+    }
     for (int64_t i = threadIdx.x; i < n; i += kWqThreads) {
         const int64_t rr = r0 + i / 128, k = kb * 128 + (i % 128);
         const float q = div_by_scale(w[rr * K + k], s, r);
@@ -163,7 +168,7 @@ hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
 hipError_t launch_quantize_weight(const WeightQuantArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.rows + a.brows - 1) / a.brows), (unsigned)(a.K / 128));
     hipLaunchKernelGGL(quantize_weight_kernel, grid, dim3(kWqThreads), 0, stream, a.w, a.codes,
-                       a.scales, a.rows, a.K, a.brows, a.pow2);
+                       a.scales, a.rows, a.K, a.brows, a.pow2 | a.e8m0, a.e8m0);
     return hipGetLastError();
 }
 

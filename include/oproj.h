@@ -75,8 +75,16 @@ typedef enum oproj_scale_mode {
  *                        [G*R, D] weight and columns 128kb..128kb+127;
  *                        scales are fp32 [ceil(G*R/128), D/128] row-major.
  *  OPROJ_WBLOCK_1x128:   scale (r, kb) per row r; fp32 [G*R, D/128] row-major.
+ *  OPROJ_WBLOCK_1x128_UE8M0: per-row power-of-two scales stored as packed
+ *                        UE8M0 words [G*R][D/512] (row r's block kb is byte
+ *                        kb % 4 of word kb / 4; [SGL] format_ue8m0 weight
+ *                        scales); only with OPROJ_SCALE_POW2 / OPROJ_SCALE_E8M0.
  * The stored scale multiplies the decoded code ([SGL] _dequant_fp8). */
-typedef enum oproj_wblock { OPROJ_WBLOCK_128x128 = 0, OPROJ_WBLOCK_1x128 = 1 } oproj_wblock;
+typedef enum oproj_wblock {
+    OPROJ_WBLOCK_128x128 = 0,
+    OPROJ_WBLOCK_1x128 = 1,
+    OPROJ_WBLOCK_1x128_UE8M0 = 2
+} oproj_wblock;
 
 /* Shape of one call ([FUSED] parameter table; [OPROJ] deep_gemm_fp8_o_proj). */
 typedef struct oproj_shape {
@@ -139,7 +147,7 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
  *                    stride_t = Gp*D, stride_g = D ([OPROJ]: live groups first,
  *                    padding sliced off).
  *  w_codes   FP8 [G*R][D] row-major (K contiguous)
- *  w_scales  fp32, blocks per `w_block`
+ *  w_scales  fp32 (or UE8M0 words), blocks per `w_block`
  *  scale_mode  OPROJ_SCALE_POW2 declares that BOTH activation and weight
  *              scales are powers of two (they are then applied by the matrix
  *              cores' block scaling); OPROJ_SCALE_E8M0 is the same with the
@@ -148,7 +156,7 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
  *  z         bf16 [T][G][R] contiguous */
 oproj_status oproj_grouped_wo_a(const oproj_shape* shape, int32_t scale_mode, const void* a_codes,
                                 const void* a_scales, const oproj_act_layout* a_layout,
-                                const void* w_codes, const float* w_scales, int32_t w_block,
+                                const void* w_codes, const void* w_scales, int32_t w_block,
                                 void* z, void* stream);
 
 /* Step a4 ([SGL] MQALayer.forward applies wo_b to z.flatten(1)):
@@ -224,7 +232,7 @@ size_t oproj_fused_workspace_bytes(const oproj_shape* shape, int64_t hidden);
  * GEMM; every argument (wo_b included) is validated before the first launch. */
 oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const void* o,
                          const int64_t* positions, const float* cos_sin, const void* w_codes,
-                         const float* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
+                         const void* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
                          void* workspace, size_t workspace_bytes, void* out, void* stream);
 
 /* Offline weight preparation ([OPROJ] compute_fp8_einsum_recipe; [SGL]
@@ -232,10 +240,11 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
  * scale per block (128x128 or 1x128 per `w_block`), scale = amax/448
  * (pow2: rounded up to a power of two; OPROJ_SCALE_E8M0 gives the same fp32
  * powers of two), code = e4m3fn(w / scale).
- *  w        fp32 [rows][K];  codes FP8 [rows][K];  scales fp32 (see oproj_wblock)
- *  K must be a multiple of 128. */
+ *  w        fp32 [rows][K];  codes FP8 [rows][K];  scales per oproj_wblock
+ *  K must be a multiple of 128 (of 512 for OPROJ_WBLOCK_1x128_UE8M0, which
+ *  also needs a power-of-two scale_mode). */
 oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
-                                   const float* w, void* codes, float* scales, void* stream);
+                                   const float* w, void* codes, void* scales, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* oproj_status_string(oproj_status status);

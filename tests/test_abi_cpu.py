@@ -195,6 +195,8 @@ def test_quantize_weight_validation(lib):
     assert f(4, 100) == E_SHAPE
     assert f(4, 128, blk=2) == E_MODE
     assert f(4, 128, mode=3) == E_MODE
+    assert f(4, 512, blk=2, mode=0) == E_MODE  # UE8M0 weight scales need power-of-two scales
+    assert f(4, 384, blk=2, mode=1) == E_SHAPE  # four blocks per word: K % 512
     assert f(4, 128, w=None) == E_NULL
     assert f(4, 128, s=0x1002) == E_ALIGN
 

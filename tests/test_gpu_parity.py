@@ -576,3 +576,42 @@ def test_fused_e8m0_equals_steps():
     zs = torch.empty_like(zf)
     ap.oproj_grouped_wo_a(shp, ap.OPROJ_SCALE_E8M0, c8, s8, None, d_wq, d_ws, 0, zs)
     assert torch.equal(zf, zs)
+
+
+# ---------------------------------------------------------------- packed UE8M0 weight scales
+def _weight_ue8m0(wmat):
+    rows, K = wmat.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=DEV)
+    words = torch.empty((rows, K // 512), dtype=torch.int32, device=DEV)
+    ap.oproj_quantize_weight(rows, K, ap.OPROJ_WBLOCK_1x128_UE8M0, ap.OPROJ_SCALE_POW2, _dev(wmat), codes, words)
+    return codes, words
+
+
+def test_weight_quant_ue8m0_words():
+    w = wl.WORKLOADS["decode"]
+    wmat = wl.wo_a_f32(w)
+    c8, w8 = _weight_ue8m0(wmat)
+    c2, s2 = gpu_weight(wmat, 1, True)
+    assert torch.equal(c8, c2)
+    qr, sr = oracle.quant_weight(wmat, 1, True)
+    assert np.array_equal(_host(w8).view(np.uint32), oracle.e8m0_pack(sr))
+
+
+@pytest.mark.parametrize("T,amode", [(64, 1), (64, 2), (300, 2), (300, 1)])
+def test_grouped_gemm_ue8m0_weights_equal_fp32_pow2(T, amode):
+    """Packed UE8M0 weight scales give the same z, bit for bit, as the same
+    powers of two stored as fp32 (few-token and tile kernels)."""
+    w = wl.WORKLOADS["decode"].scaled(T)
+    o, tab = wl.attn_out(w), wl.table(w)
+    pos = wl.uniform_int(wl.seed_of(79, T), T, 0, w.max_pos)
+    c2, s2, c8, s8 = _quant_both_modes(w, o, pos, tab)
+    codes, scales = (c2, s2) if amode == 1 else (c8, s8)
+    wmat = wl.wo_a_f32(w)
+    wc, ws32 = gpu_weight(wmat, 1, True)
+    wc8, ws8 = _weight_ue8m0(wmat)
+    shp = _shape(w, T)
+    za = torch.empty((T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    zb = torch.empty_like(za)
+    ap.oproj_grouped_wo_a(shp, amode, codes, scales, None, wc, ws32, ap.OPROJ_WBLOCK_1x128, za)
+    ap.oproj_grouped_wo_a(shp, amode, codes, scales, None, wc8, ws8, ap.OPROJ_WBLOCK_1x128_UE8M0, zb)
+    assert torch.equal(za, zb)
