@@ -26,6 +26,7 @@ from ._native import (  # noqa: F401
     oproj_dense_bf16_gemm,
     oproj_fused,
     oproj_fused_bf16,
+    oproj_fused_decode,
     oproj_fused_bf16_workspace_bytes,
     oproj_fused_workspace_bytes,
     oproj_grouped_wo_a,

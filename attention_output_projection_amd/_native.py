@@ -124,6 +124,7 @@ def load_library():
             "oproj_fused_bf16_workspace_bytes": (SZ, [SP, I64]),
             "oproj_fused_bf16": (I32, [SP, P, P, P, P, P, I64, P, SZ, P, P]),
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
+            "oproj_fused_decode": (I32, [SP, I32, P, P, P, P, P, I32, P, SZ, P, P]),
             "oproj_quantize_weight": (I32, [I64, I64, I32, I32, P, P, P, P]),
             "oproj_status_string": (ctypes.c_char_p, [I32]),
             "oproj_version": (ctypes.c_char_p, []),
@@ -220,6 +221,14 @@ def oproj_fused(shape: Shape, scale_mode: int, o, positions, cos_sin, w_codes, w
         _ptr(w_scales), w_block, _ptr(wo_b), hidden, _ptr(workspace), workspace_bytes, _ptr(out),
         _stream(stream))
     _check("oproj_fused", st)
+
+
+def oproj_fused_decode(shape: Shape, scale_mode: int, o, positions, cos_sin, w_codes, w_scales, w_block: int,
+                       workspace, workspace_bytes: int, z, stream=None) -> None:
+    st = load_library().oproj_fused_decode(
+        ctypes.byref(shape._c()), scale_mode, _ptr(o), _ptr(positions), _ptr(cos_sin), _ptr(w_codes),
+        _ptr(w_scales), w_block, _ptr(workspace), workspace_bytes, _ptr(z), _stream(stream))
+    _check("oproj_fused_decode", st)
 
 
 def oproj_fused_bf16_workspace_bytes(shape: Shape, hidden: int = 0) -> int:

@@ -371,6 +371,38 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
                                  out, stream);
 }
 
+oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                                const int64_t* positions, const float* cos_sin, const void* w_codes,
+                                const void* w_scales, int32_t w_block, void* workspace,
+                                size_t workspace_bytes, void* z, void* stream) {
+    oproj_status st = check_shape(shape, true);
+    if (st != OPROJ_OK) return st;
+    if (!valid_mode(scale_mode)) return OPROJ_E_MODE;
+    if (!valid_wblock(w_block, scale_mode)) return OPROJ_E_MODE;
+    if (shape->T > 64 || shape->n_groups > 256) return OPROJ_E_SHAPE;
+    if (shape->heads_per_group != 2 && shape->heads_per_group % 4 != 0) return OPROJ_E_MODE;
+    if (shape->T == 0) return OPROJ_OK;
+    if (!o || !positions || !cos_sin || !w_codes || !w_scales || !workspace || !z) return OPROJ_E_NULL;
+    if (workspace_bytes < oproj_fused_workspace_bytes(shape, 0)) return OPROJ_E_SHAPE;
+    if (!aligned16(workspace)) return OPROJ_E_ALIGN;
+    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups, D = (size_t)shape->heads_per_group * 512;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* codes = ws;
+    float* scales = reinterpret_cast<float*>(ws + round_up(T * G * D));
+    oproj::RopeQuantArgs qa;
+    oproj::GroupedGemmArgs ga;
+    if ((st = prep_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, &qa)) != OPROJ_OK)
+        return st;
+    if ((st = prep_gemm(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block, z, &ga)) !=
+        OPROJ_OK)
+        return st;
+    bool launched = false;
+    if ((st = from_hip(oproj::launch_fused_decode(qa, ga, static_cast<hipStream_t>(stream), &launched))) !=
+        OPROJ_OK)
+        return st;
+    return launched ? OPROJ_OK : OPROJ_E_SHAPE;
+}
+
 oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
                                    const float* w, void* codes, void* scales, void* stream) {
     if (rows < 0 || K < 128 || K % 128 != 0) return OPROJ_E_SHAPE;

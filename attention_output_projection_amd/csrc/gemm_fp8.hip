@@ -33,10 +33,14 @@
 //    partial tiles summed through LDS at the end.  The weight stream is the
 //    cost at small T; the deep ring keeps enough of it in flight.
 // Both remap workgroups so that tiles of one group land on one XCD (a group's
-// activations and weights then stay in that XCD's L2).
+// activations and weights then stay in that XCD's L2).  A third kernel runs
+// the decode kernel's grid with the quantisation (steps a1 + a2) in front:
+// each workgroup quantises its share of its group into a workspace, the
+// group's workgroups meet at a barrier of their own, then each runs its tile.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
+#include "rq_item.hpp"
 
 #ifndef OPROJ_DEC_W_NT
 #define OPROJ_DEC_W_NT 1
@@ -316,10 +320,58 @@ constexpr int DVM = 9;  // copy instructions per copying wave per stage
 constexpr int DPROW = DBN + 4;  // fp32 per row of an epilogue partial tile (pad against bank conflicts)
 static_assert(DKS * DBM * DPROW * 4 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
 
+// Barrier state of the one-launch decode path: one 64-bit word per group, on
+// a cache line of its own (zero when the library loads).  Fields, low bit
+// first: arrivals at the current barrier (9 bits), the sum of the arrivals'
+// XCD numbers (12 bits) and of their squares (16 bits), whether the previous
+// barrier's arrivals ran on more than one XCD (1 bit), and the count of
+// barriers the group has completed (its epoch, the top 26 bits).  One
+// returning atomic add per arrival; the last arrival replaces the word with
+// the next epoch and its XCD flag in a second add, so every launch leaves
+// the word ready for the next one whatever its group size.
+constexpr int kMaxFusedGroups = 256;
+constexpr int kSyncStride = 16;  // 128-byte cache line
+__device__ uint64_t g_group_sync[kSyncStride * kMaxFusedGroups];
+constexpr int kGroupSpinLimit = 4096;  // bounded wait: a missing workgroup is covered by a fallback
+constexpr int kSyncSum = 9, kSyncSq = 21, kSyncMixed = 37, kSyncEpoch = 38;
+
+// XCD (XCC) this wave runs on.
+__device__ __forceinline__ uint64_t xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xFu; }
+
+// Arrive at group g's barrier of n (at most 256) workgroups and wait for the
+// others.  Returns 0 when every workgroup of the group arrived and all ran on
+// one XCD, 1 when they arrived from several XCDs, 2 when the wait gave up
+// (the caller then does the missing work itself).  Called by one thread.
+__device__ int group_barrier(int64_t g, int64_t n) {
+    uint64_t* word = &g_group_sync[kSyncStride * g];
+    const uint64_t x = xcc_id();
+    const uint64_t inc = 1ull + (x << kSyncSum) + ((x * x) << kSyncSq);
+    const uint64_t old = __hip_atomic_fetch_add(word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t epoch = old >> kSyncEpoch;
+    if ((old & ((1ull << kSyncSum) - 1)) == (uint64_t)(n - 1)) {
+        const uint64_t fin = old + inc;
+        const uint64_t s1 = (fin >> kSyncSum) & ((1ull << (kSyncSq - kSyncSum)) - 1);
+        const uint64_t s2 = (fin >> kSyncSq) & ((1ull << (kSyncMixed - kSyncSq)) - 1);
+        const uint64_t mixed = (uint64_t)n * s2 != s1 * s1;  // equal only when every x is the same
+        const uint64_t next = ((epoch + 1) << kSyncEpoch) | (mixed << kSyncMixed);
+        __hip_atomic_fetch_add(word, next - fin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return (int)mixed;
+    }
+    for (int it = 0; it < kGroupSpinLimit; ++it) {
+        const uint64_t w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w >> kSyncEpoch) != epoch) return (int)((w >> kSyncMixed) & 1);
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return 2;
+}
+
 // One workgroup's output tile (the whole decode pipeline); ring is the
-// workgroup's LDS.
-template <bool MX, bool W1>
-__device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DKS][DNS][DSTAGE]) {
+// workgroup's LDS.  QCH > 0 is the one-launch path: the workgroup also
+// quantises its share of the group's activations (items of QCH heads, with
+// the rq::Params q) before the GEMM reads them.
+template <bool MX, bool W1, int QCH>
+__device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DKS][DNS][DSTAGE],
+                                            const rq::Params& q) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group within the tile
@@ -373,11 +425,18 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         kshl = p.wkshift;
     }
     const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
-    auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
+    // step i's copies: the activation slab and the scales (5 instructions),
+    // the weight slab (4)
+    auto issue_a = [&](int64_t i, int slot) __attribute__((always_inline)) {
         const int64_t kb = kb0 + i;
         const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16s(abase + kb * 128, off[j], st + (32 * wave + 8 * j) * 128);
+        dma4(ssrc + (kb >> kshl) * sstep, st + 16384 + 256 * wave);
+    };
+    auto issue_w = [&](int64_t i, int slot) __attribute__((always_inline)) {
+        const int64_t kb = kb0 + i;
+        const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (OPROJ_DEC_W_NT)
@@ -385,13 +444,66 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
             else
                 dma16s(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
         }
-        dma4(ssrc + (kb >> kshl) * sstep, st + 16384 + 256 * wave);
+    };
+    auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
+        issue_a(i, slot);
+        issue_w(i, slot);
     };
 
-    if (copier) {
+    if constexpr (QCH == 0) {
+        if (copier) {
 #pragma unroll
-        for (int s = 0; s < DNS - 1; ++s)
-            if (s < nkb) issue(s, s);
+            for (int s = 0; s < DNS - 1; ++s)
+                if (s < nkb) issue(s, s);
+        }
+    } else {
+        static_assert(QCH == 0 || DNS == 4, "the one-launch waits below assume a 4-stage ring");
+        // One-launch path (the launcher guarantees nkb >= DNS and one M-tile).
+        // The weights of the first DNS-1 steps do not depend on the
+        // quantisation: the copying waves request them first.
+        if (copier) {
+#pragma unroll
+            for (int s = 0; s < DNS - 1; ++s) issue_w(s, s);
+        }
+        // All eight waves then quantise this workgroup's share of the group's
+        // items (token, head chunk) into the workspace; a copying wave's
+        // first wait also covers its weight copies, which were issued first.
+        const rq::Wave<QCH> qwv(q, lane);
+        auto quantise = [&](int64_t first, int64_t step) __attribute__((always_inline)) {
+            const int64_t items = q.T * q.nchunk;
+            for (int64_t it = first; it < items; it += step) {
+                const int64_t t = it / q.nchunk, chunk = it % q.nchunk;
+                uint4 raw[QCH];
+                qwv.load_rows(t, g, chunk, raw);
+                const int64_t ps = q.pos[t];
+                float4 cs, sn;
+                qwv.load_table(ps, cs, sn);
+                // system-coherent stores: visible to the group's readers on
+                // this XCD through L2 and on any other XCD through memory
+                qwv.template process<true>(t, g, chunk, ps, raw, cs, sn);
+            }
+            wait_vmcnt<0>();  // the stores have completed before the arrival
+        };
+        quantise(nt * 8 + (tid >> 6), p.ntiles * 8);
+        __shared__ int sync_state;
+        __syncthreads();
+        if (tid == 0) sync_state = group_barrier(g, p.ntiles);
+        __syncthreads();
+        if (sync_state == 2) {
+            // a workgroup of the group did not arrive in time: quantise the
+            // whole group here (the same bytes the others write)
+            quantise(tid >> 6, 8);
+            __syncthreads();
+        }
+        // A reader's L2 on an XCD other than a writer's may hold stale lines
+        // of the workspace from an earlier launch: drop them.  Only then: the
+        // invalidation also drops the lines that the XCD's other workgroups
+        // are sharing, which costs far more than the instruction.
+        if (sync_state != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (copier) {
+#pragma unroll
+            for (int s = 0; s < DNS - 1; ++s) issue_a(s, s);
+        }
     }
 
     v4f acc[4];
@@ -405,7 +517,19 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         // this wave's copies of stage i have landed; the copies of the stages
         // after it that were issued (at most DNS-2, none past the group's
         // last block) may still be in flight
-        if (copier) wait_ahead<DNS - 2, DVM>(nkb - 1 - i);
+        if (copier) {
+            if (QCH > 0 && i < DNS - 1) {
+                // the prologue issued the weights of steps 0..DNS-2 before their
+                // activations: after step i's activations come those of steps
+                // i+1..DNS-2 (5 instructions each) and the i whole steps issued
+                // by the loop so far
+                if (i == 0) wait_vmcnt<5 * (DNS - 2)>();
+                else if (i == 1) wait_vmcnt<5 * (DNS - 3) + DVM>();
+                else wait_vmcnt<5 * (DNS - 4 > 0 ? DNS - 4 : 0) + 2 * DVM>();
+            } else {
+                wait_ahead<DNS - 2, DVM>(nkb - 1 - i);
+            }
+        }
         __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence)
         if (copier && i + DNS - 1 < nkb) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
         if (i >= nkb) continue;        // uniform per wave group
@@ -477,7 +601,16 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
 template <bool MX, bool W1>
 __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
-    decode_tile<MX, W1>(p, ring);
+    const rq::Params none{};
+    decode_tile<MX, W1, 0>(p, ring, none);
+}
+
+// One launch for a decode step: quantisation (spread over the GEMM's own
+// workgroups, a barrier per group) and the grouped GEMM.
+template <bool MX, bool W1, int QCH>
+__global__ __launch_bounds__(DKS * 256) void fused_decode_kernel(GParams p, rq::Params q) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
+    decode_tile<MX, W1, QCH>(p, ring, q);
 }
 
 void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
@@ -496,6 +629,65 @@ void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
 }
 
 }  // namespace
+
+
+hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a, hipStream_t stream,
+                               bool* launched) {
+    *launched = false;
+    // eligible: one M-tile, every K-group long enough for the prologue, a
+    // two- or four-head quantisation item, and every workgroup resident at
+    // once (one per CU) so that the per-group barriers complete without the
+    // fallback
+    const int64_t KB = a.D / 128;
+    const int64_t ntiles = (a.R + DBN - 1) / DBN;
+    if (a.T > DBM || KB / DKS < DNS || a.G > kMaxFusedGroups) return hipSuccess;
+    const int ch = rq::heads_per_item(qa.hpg);
+    if (ch != 2 && ch != 4) return hipSuccess;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipSuccess;
+    if (a.G * ntiles > cus) return hipSuccess;
+    GParams p;
+    p.a = a.a;
+    p.sa = static_cast<const float*>(a.sa);
+    p.w = a.w;
+    p.sw = static_cast<const float*>(a.sw);
+    p.z = a.z;
+    p.T = a.T;
+    p.G = a.G;
+    p.D = a.D;
+    p.R = a.R;
+    p.KB = KB;
+    p.st = a.lay.stride_t;
+    p.sg = a.lay.stride_g;
+    p.sst = a.lay.s_stride_t;
+    p.ssg = a.lay.s_stride_g;
+    p.sskb = a.lay.s_stride_kb;
+    p.w_shift = a.w_1x128 ? 0 : 7;
+    p.e8 = a.a_e8m0;
+    p.kshift = a.a_e8m0 ? 2 : 0;
+    p.we8 = a.w_e8m0;
+    p.wkshift = a.w_e8m0 ? 2 : 0;
+    p.kbw = a.w_e8m0 ? KB / 4 : KB;
+    p.mtiles = 1;
+    p.ntiles = ntiles;
+    const rq::Params q = rq::make_params(qa, ch);
+    const dim3 grid((unsigned)(a.G * ntiles)), block(DKS * 256);
+#define OPROJ_FUSED_LAUNCH(MXV, W1V, CHV) \
+    hipLaunchKernelGGL((fused_decode_kernel<MXV, W1V, CHV>), grid, block, 0, stream, p, q)
+#define OPROJ_FUSED_CH(MXV, W1V) \
+    if (ch == 2) OPROJ_FUSED_LAUNCH(MXV, W1V, 2); else OPROJ_FUSED_LAUNCH(MXV, W1V, 4)
+    if (a.mx) {
+        if (a.w_1x128) { OPROJ_FUSED_CH(true, true); } else { OPROJ_FUSED_CH(true, false); }
+    } else {
+        if (a.w_1x128) { OPROJ_FUSED_CH(false, true); } else { OPROJ_FUSED_CH(false, false); }
+    }
+#undef OPROJ_FUSED_CH
+#undef OPROJ_FUSED_LAUNCH
+    *launched = true;
+    return hipGetLastError();
+}
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     GParams p;

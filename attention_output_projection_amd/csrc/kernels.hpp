@@ -50,6 +50,14 @@ struct GroupedGemmArgs {
 };
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t s);
 
+// One launch for both steps at few tokens (quantisation into the default
+// layout of q's buffers, then the grouped GEMM reading them).  *launched is
+// false, and nothing is enqueued, when the shape does not fit that path.
+// Launches of this path on one GPU must not overlap in time (they share the
+// per-group barrier words the library holds on each device).
+hipError_t launch_fused_decode(const RopeQuantArgs& q, const GroupedGemmArgs& a, hipStream_t s,
+                               bool* launched);
+
 struct RopeBf16Args {
     int64_t T, G, hpg, max_pos;
     const uint16_t* o;         // bf16 [T][G*hpg][512]

@@ -93,7 +93,10 @@ struct Wave {
             sn = *reinterpret_cast<const float4*>(row + 32);
         }
     }
-    // rotate, reduce, scale, convert and store one item
+    // rotate, reduce, scale, convert and store one item; SYS stores with
+    // system-scope coherence (written through to memory, for readers in other
+    // workgroups of the same launch), else non-temporal codes
+    template <bool SYS = false>
     __device__ __forceinline__ void process(int64_t t, int64_t g, int64_t chunk, int64_t ps, const uint4* raw,
                                             float4 cs, float4 sn) const {
         const bool bad = (ps < 0) | (ps >= p.max_pos);
@@ -149,12 +152,20 @@ struct Wave {
                            e3 = __shfl(e, (lane + 48) & 63);
             if (c == 0 && li < CH) {
                 const int64_t hw = chunk * CH + li;  // head within the group = word index
-                static_cast<uint32_t*>(p.scales)[t * p.sst + g * p.ssg + hw * p.sskb] =
-                    e | (e1 << 8) | (e2 << 16) | (e3 << 24);
+                uint32_t* dst = static_cast<uint32_t*>(p.scales) + t * p.sst + g * p.ssg + hw * p.sskb;
+                const uint32_t word = e | (e1 << 8) | (e2 << 16) | (e3 << 24);
+                if constexpr (SYS)
+                    __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                else
+                    *dst = word;
             }
         } else if (li < CH) {
             const int64_t kb = (chunk * CH + li) * 4 + c;
-            static_cast<float*>(p.scales)[t * p.sst + g * p.ssg + kb * p.sskb] = s;
+            float* dst = static_cast<float*>(p.scales) + t * p.sst + g * p.ssg + kb * p.sskb;
+            if constexpr (SYS)
+                __hip_atomic_store(dst, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            else
+                *dst = s;
         }
 
         uint8_t* dst = p.codes + t * p.st + g * p.sg + chunk * CH * 512 + 8 * lane;
@@ -172,7 +183,11 @@ struct Wave {
             u32x2 x;
             x.x = w0;
             x.y = w1;
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(dst + (int64_t)j * 512));
+            if constexpr (SYS)
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + (int64_t)j * 512),
+                                   (uint64_t)w0 | ((uint64_t)w1 << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            else
+                __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(dst + (int64_t)j * 512));
         }
     }
 };

@@ -65,6 +65,7 @@ KERNEL_SOURCES = {
     "inv_rope_quant": ("rope_quant.hip", "rq_item.hpp", "device_common.hpp"),
     "grouped_wo_a": ("gemm_fp8.hip", "lds_dma.hpp", "device_common.hpp"),
     "wo_b": ("gemm_bf16.hip", "lds_dma.hpp", "device_common.hpp"),
+    "fused_decode": ("gemm_fp8.hip", "rq_item.hpp", "lds_dma.hpp", "device_common.hpp"),
 }
 
 
@@ -247,8 +248,9 @@ def main() -> int:
     ap_.add_argument("--kernel-reps", type=int, default=50, help="graph replays per kernel timing")
     ap_.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
     ap_.add_argument("--no-cpu-baseline", action="store_true")
-    ap_.add_argument("--path", default="fp8", choices=["fp8", "bf16"],
-                     help="fp8: the quantised path (default); bf16: the unquantised variant")
+    ap_.add_argument("--path", default="fp8", choices=["fp8", "bf16", "one-launch"],
+                     help="fp8: the quantised path (default); bf16: the unquantised variant; one-launch: "
+                          "the quantised path as one kernel (oproj_fused_decode; decode-sized batches)")
     ap_.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                      help="only run plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap_.parse_args()
@@ -274,6 +276,10 @@ def main() -> int:
     if args.path == "bf16":
         return bench_bf16(args, w, torch, ap, wl, dev)
     log(f"workload {w.name}: T={w.T} G={w.n_groups} hpg={w.heads_per_group} D={w.D} R={w.o_lora_rank}")
+    one_launch = args.path == "one-launch"
+    if one_launch and (w.T > 64 or w.hidden):
+        print("--path one-launch takes a decode-sized workload without wo_b (T <= 64)", file=sys.stderr)
+        return 2
 
     # ---------------------------------------------------------------- inputs
     o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
@@ -322,7 +328,11 @@ def main() -> int:
     def wo_b(c):
         ap.oproj_dense_bf16_gemm(w.T, w.hidden, wrows, c["z"], c["wob"], c["y"])
 
-    def step(c):  # the whole path: one oproj_fused call
+    def step(c):  # the whole path: one oproj_fused (or oproj_fused_decode) call
+        if one_launch:
+            ap.oproj_fused_decode(shp, mode, c["o"], d_pos, d_tab, c["wq"], c["ws"], wblock, c["work"],
+                                  ws_bytes, c["z"])
+            return
         out = c["y"] if wob is not None else c["z"]
         ap.oproj_fused(shp, mode, c["o"], d_pos, d_tab, c["wq"], c["ws"], wblock,
                        c.get("wob"), hidden, c["work"], ws_bytes, out)
@@ -413,11 +423,18 @@ def main() -> int:
     if t_wob is not None:
         fl = 2 * w.T * w.hidden * wrows
         kernels["wo_b"] = {"us": t_wob, "bound": "mfma", "flops": fl, "TFLOP/s": fl / (t_wob * 1e6)}
+    if one_launch:
+        # the one kernel of the step; its bytes are both steps' (the codes and
+        # scales still go through the workspace)
+        t_one = kernel_time_us(g_step)
+        nb = kernel_bytes_quant(w) + kernel_bytes_gemm(w)
+        kernels["fused_decode"] = {"us": t_one, "bound": "hbm", "bytes": nb, "GB/s": nb / (t_one * 1e3)}
+        log(f"one-launch kernel: {t_one:.2f} us")
 
-    dominant = max(kernels, key=lambda k: kernels[k]["us"])
+    dominant = "fused_decode" if one_launch else max(kernels, key=lambda k: kernels[k]["us"])
     kd = kernels[dominant]
     sha = source_sha(*KERNEL_SOURCES[dominant])
-    if dominant == "inv_rope_quant":
+    if dominant in ("inv_rope_quant", "fused_decode"):
         achieved, peak, unit, bound = kd["GB/s"], HBM_PEAK_GBS, "GB/s", "hbm"
     elif dominant == "grouped_wo_a":
         if gemm_bound == "hbm":
@@ -454,6 +471,7 @@ def main() -> int:
                                + (f" hidden={w.hidden}" if w.hidden else "")
                                + f" scales={'pow2' if w.pow2 else 'fp32'}",
                    "global_batch": w.T, "parallelism": "single GPU",
+                   "path": "one kernel (oproj_fused_decode)" if one_launch else "oproj_fused",
                    "step_TFLOP/s": gemm_tflops, "copies_rotated": copies},
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},

@@ -235,6 +235,28 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
                          const void* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
                          void* workspace, size_t workspace_bytes, void* out, void* stream);
 
+/* Steps a1 + a2 + a3 of oproj_fused (wo_b == NULL) in ONE kernel launch, for
+ * decode-sized batches, where the launch and the quantisation round trip sit
+ * on the per-token critical path ([SGL] the wo_a decode path; [FUSED] feeds
+ * the grouped GEMM directly).  Each workgroup first quantises its share of
+ * its group's activations into the workspace, meets the group's other
+ * workgroups at a barrier, then runs its output tile of the grouped GEMM.
+ * Arguments, workspace (oproj_fused_workspace_bytes(shape, 0)) and result are
+ * those of oproj_fused with wo_b == NULL; z is bit-identical to it.
+ * Supported: T <= 64, n_groups <= 256, heads_per_group 2 or a multiple of 4,
+ * D / 128 >= 8, and n_groups * ceil(o_lora_rank / 64) workgroups no more than
+ * the device's compute units (every workgroup resident at once); otherwise
+ * OPROJ_E_SHAPE (or OPROJ_E_MODE for the head geometry) and nothing is
+ * enqueued.
+ * Concurrency: calls on one device must not overlap in time, on any streams:
+ * they share the library's per-group barrier words on that device.  A
+ * workgroup that waits too long at its barrier quantises its whole group
+ * itself, so a slow neighbour costs time, never correctness. */
+oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                                const int64_t* positions, const float* cos_sin, const void* w_codes,
+                                const void* w_scales, int32_t w_block, void* workspace,
+                                size_t workspace_bytes, void* z, void* stream);
+
 /* Offline weight preparation ([OPROJ] compute_fp8_einsum_recipe; [SGL]
  * _setup_fp8_wo_a_scales): quantise fp32 w[rows][K] to FP8 codes with one
  * scale per block (128x128 or 1x128 per `w_block`), scale = amax/448

@@ -188,6 +188,29 @@ def test_fused_workspace_and_validation(lib):
     assert fused(_shape(T=0), 0) == E_OK
 
 
+def test_fused_decode_validation(lib):
+    """The one-launch entry point's checks, all made before anything touches
+    the device: shape limits, head geometry, pointers, workspace size."""
+    shp = _shape(T=64, n_groups=16, heads_per_group=8, o_lora_rank=1024, max_pos=32768)
+    n0 = ap.oproj_fused_workspace_bytes(shp, 0)
+    P = 0x1000
+
+    def dec(shape, ws_bytes=n0, mode=0, wblock=0, ws=P, o=P, z=P):
+        return _raw("oproj_fused_decode", ctypes.byref(shape._c()), mode, o, P, P, P, P, wblock, ws, ws_bytes,
+                    z, None)
+
+    assert dec(_shape(T=0), 0, o=None, z=None, ws=None) == E_OK
+    assert dec(_shape(T=65, n_groups=1, heads_per_group=8, o_lora_rank=64)) == E_SHAPE
+    assert dec(_shape(T=8, n_groups=257, heads_per_group=8, o_lora_rank=64)) == E_SHAPE
+    assert dec(_shape(T=8, n_groups=2, heads_per_group=1, o_lora_rank=64)) == E_MODE
+    assert dec(shp, o=None) == E_NULL
+    assert dec(shp, z=None) == E_NULL
+    assert dec(shp, n0 - 1) == E_SHAPE
+    assert dec(shp, ws=BAD) == E_ALIGN
+    assert dec(shp, mode=3) == E_MODE
+    assert dec(shp, mode=0, wblock=2) == E_MODE
+
+
 def test_quantize_weight_validation(lib):
     f = lambda rows, K, blk=0, mode=0, w=0x1000, c=0x1000, s=0x1000: _raw(
         "oproj_quantize_weight", rows, K, blk, mode, w, c, s, None)
