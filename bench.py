@@ -246,6 +246,8 @@ def main() -> int:
     ap_.add_argument("--workload", default="decode", choices=["decode", "prefill", "pow2", "full", "tiny"])
     ap_.add_argument("--copies", type=int, default=0, help="input/weight copies rotated (0: auto)")
     ap_.add_argument("--kernel-reps", type=int, default=50, help="graph replays per kernel timing")
+    ap_.add_argument("--pct-reps", type=int, default=50,
+                     help="individually timed graph replays for the p10/p50/p90 figures")
     ap_.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
     ap_.add_argument("--no-cpu-baseline", action="store_true")
     ap_.add_argument("--path", default="fp8", choices=["fp8", "bf16", "one-launch"],
@@ -404,6 +406,27 @@ def main() -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (args.kernel_reps * copies)
 
+    def percentiles_us(g):
+        """p10/p50/p90 of the per-launch time over individually timed replays
+        (each replay runs the rotation of `copies` launches)."""
+        g.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.pct_reps)]
+        for a, b in evs:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        v = np.array([a.elapsed_time(b) * 1e3 / copies for a, b in evs])
+        return [float(np.percentile(v, q)) for q in (10, 50, 90)]
+
+    pct = {"step": percentiles_us(g_step), "inv_rope_quant": percentiles_us(g_quant),
+           "grouped_wo_a": percentiles_us(g_gemm)}
+    if g_wob is not None:
+        pct["wo_b"] = percentiles_us(g_wob)
+    log("p10/p50/p90 us: " + ", ".join(f"{k} {a:.2f}/{b:.2f}/{c:.2f}" for k, (a, b, c) in pct.items()))
+
     t_quant = kernel_time_us(g_quant)
     t_gemm = kernel_time_us(g_gemm)
     t_wob = kernel_time_us(g_wob) if g_wob is not None else None
@@ -477,6 +500,7 @@ def main() -> int:
                      "frac": achieved / peak, "traffic": traffic},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "p10_p50_p90_us": pct,
     }
     print(json.dumps(result), flush=True)
     return 0
