@@ -125,6 +125,7 @@ def load_library():
             "oproj_fused_bf16": (I32, [SP, P, P, P, P, P, I64, P, SZ, P, P]),
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
             "oproj_fused_decode": (I32, [SP, I32, P, P, P, P, P, I32, P, SZ, P, P]),
+            "oproj_fused_decode_unsupported": (ctypes.c_char_p, [SP, I32, I32]),
             "oproj_quantize_weight": (I32, [I64, I64, I32, I32, P, P, P, P]),
             "oproj_status_string": (ctypes.c_char_p, [I32]),
             "oproj_version": (ctypes.c_char_p, []),
@@ -229,6 +230,12 @@ def oproj_fused_decode(shape: Shape, scale_mode: int, o, positions, cos_sin, w_c
         ctypes.byref(shape._c()), scale_mode, _ptr(o), _ptr(positions), _ptr(cos_sin), _ptr(w_codes),
         _ptr(w_scales), w_block, _ptr(workspace), workspace_bytes, _ptr(z), _stream(stream))
     _check("oproj_fused_decode", st)
+
+
+def oproj_fused_decode_unsupported(shape: Shape, scale_mode: int = 0, w_block: int = 0):
+    """None when oproj_fused_decode can take this shape on the current device, else the reason."""
+    r = load_library().oproj_fused_decode_unsupported(ctypes.byref(shape._c()), scale_mode, w_block)
+    return None if r is None else r.decode()
 
 
 def oproj_fused_bf16_workspace_bytes(shape: Shape, hidden: int = 0) -> int:

@@ -403,6 +403,14 @@ oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, co
     return launched ? OPROJ_OK : OPROJ_E_SHAPE;
 }
 
+const char* oproj_fused_decode_unsupported(const oproj_shape* shape, int32_t scale_mode, int32_t w_block) {
+    if (check_shape(shape, true) != OPROJ_OK) return "invalid shape";
+    if (!valid_mode(scale_mode) || !valid_wblock(w_block, scale_mode))
+        return "unsupported scale mode or weight block mode";
+    if (shape->T == 0) return nullptr;  // the entry point returns at once
+    return oproj::fused_decode_unfit(shape->T, shape->n_groups, shape->heads_per_group, shape->o_lora_rank);
+}
+
 oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
                                    const float* w, void* codes, void* scales, void* stream) {
     if (rows < 0 || K < 128 || K % 128 != 0) return OPROJ_E_SHAPE;

@@ -631,23 +631,32 @@ void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
 }  // namespace
 
 
-hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a, hipStream_t stream,
-                               bool* launched) {
-    *launched = false;
+const char* fused_decode_unfit(int64_t T, int64_t G, int64_t hpg, int64_t R) {
     // eligible: one M-tile, every K-group long enough for the prologue, a
     // two- or four-head quantisation item, and every workgroup resident at
     // once (one per CU) so that the per-group barriers complete without the
     // fallback
-    const int64_t KB = a.D / 128;
-    const int64_t ntiles = (a.R + DBN - 1) / DBN;
-    if (a.T > DBM || KB / DKS < DNS || a.G > kMaxFusedGroups) return hipSuccess;
-    const int ch = rq::heads_per_item(qa.hpg);
-    if (ch != 2 && ch != 4) return hipSuccess;
+    if (T > DBM) return "more than 64 tokens";
+    if (G > kMaxFusedGroups) return "more than 256 groups";
+    const int ch = rq::heads_per_item(hpg);
+    if (ch != 2 && ch != 4) return "heads_per_group is neither 2 nor a multiple of 4";
+    if (hpg * 512 / 128 / DKS < DNS) return "head dimension too short for the copy pipeline";
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return hipSuccess;
-    if (a.G * ntiles > cus) return hipSuccess;
+        return "no device to query";
+    if (G * ((R + DBN - 1) / DBN) > cus)
+        return "more workgroups (n_groups x o_lora_rank / 64) than compute units";
+    return nullptr;
+}
+
+hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a, hipStream_t stream,
+                               bool* launched) {
+    *launched = false;
+    if (fused_decode_unfit(a.T, a.G, qa.hpg, a.R)) return hipSuccess;
+    const int64_t KB = a.D / 128;
+    const int64_t ntiles = (a.R + DBN - 1) / DBN;
+    const int ch = rq::heads_per_item(qa.hpg);
     GParams p;
     p.a = a.a;
     p.sa = static_cast<const float*>(a.sa);

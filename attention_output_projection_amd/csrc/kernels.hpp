@@ -57,6 +57,9 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t s);
 // per-group barrier words the library holds on each device).
 hipError_t launch_fused_decode(const RopeQuantArgs& q, const GroupedGemmArgs& a, hipStream_t s,
                                bool* launched);
+// Why that path cannot take a call of this shape on the current device
+// (static text), or nullptr when it can.
+const char* fused_decode_unfit(int64_t T, int64_t G, int64_t hpg, int64_t R);
 
 struct RopeBf16Args {
     int64_t T, G, hpg, max_pos;

@@ -257,6 +257,14 @@ oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, co
                                 const void* w_scales, int32_t w_block, void* workspace,
                                 size_t workspace_bytes, void* z, void* stream);
 
+/* Whether oproj_fused_decode can take a call of this shape and these modes on
+ * the current device: NULL when it can, else a short reason (static storage),
+ * like the eligibility check that reports why a layer cannot take the fused
+ * inverse RoPE + FP8 output, or None ([OPROJ] rope_quant_unsupported_reason).
+ * Pointers are not examined; T == 0 is reported as supported.  Queries the
+ * current device's compute-unit count. */
+const char* oproj_fused_decode_unsupported(const oproj_shape* shape, int32_t scale_mode, int32_t w_block);
+
 /* Offline weight preparation ([OPROJ] compute_fp8_einsum_recipe; [SGL]
  * _setup_fp8_wo_a_scales): quantise fp32 w[rows][K] to FP8 codes with one
  * scale per block (128x128 or 1x128 per `w_block`), scale = amax/448

@@ -211,6 +211,23 @@ def test_fused_decode_validation(lib):
     assert dec(shp, mode=0, wblock=2) == E_MODE
 
 
+def test_fused_decode_unsupported_reasons(lib):
+    """The eligibility query's static reasons (no device needed for these)."""
+    q = ap.oproj_fused_decode_unsupported
+    assert q(_shape(T=65, n_groups=2, heads_per_group=8, o_lora_rank=64)) == "more than 64 tokens"
+    assert q(_shape(T=8, n_groups=257, heads_per_group=8, o_lora_rank=64)) == "more than 256 groups"
+    assert "heads_per_group" in q(_shape(T=8, n_groups=2, heads_per_group=1, o_lora_rank=64))
+    assert q(_shape(T=8, n_groups=2, heads_per_group=8, o_lora_rank=64), 3) == \
+        "unsupported scale mode or weight block mode"
+    assert q(_shape(T=8, n_groups=2, heads_per_group=8, o_lora_rank=64), 0, 2) == \
+        "unsupported scale mode or weight block mode"
+    assert q(_shape(T=8, n_groups=2, heads_per_group=8, o_lora_rank=10)) == "invalid shape"
+    # a shape that passes the static checks reaches the device query (a string
+    # either way: "no device to query" here, None or the CU limit on a GPU)
+    r = q(_shape(T=8, n_groups=2, heads_per_group=8, o_lora_rank=64))
+    assert r is None or isinstance(r, str)
+
+
 def test_quantize_weight_validation(lib):
     f = lambda rows, K, blk=0, mode=0, w=0x1000, c=0x1000, s=0x1000: _raw(
         "oproj_quantize_weight", rows, K, blk, mode, w, c, s, None)

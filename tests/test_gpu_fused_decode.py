@@ -194,6 +194,16 @@ def test_one_launch_graph_replays():
         torch.cuda.synchronize()
 
 
+def test_eligibility_query_agrees_with_the_entry_point():
+    """None for the decode batch; the compute-unit reason for a grid wider
+    than the device, which the entry point refuses."""
+    dec = ap.Shape(T=64, n_groups=16, heads_per_group=8, o_lora_rank=1024, max_pos=32768)
+    assert ap.oproj_fused_decode_unsupported(dec) is None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wide = ap.Shape(T=8, n_groups=cus // 16 + 1, heads_per_group=8, o_lora_rank=1024, max_pos=8192)
+    assert "compute units" in ap.oproj_fused_decode_unsupported(wide)
+
+
 def test_one_launch_refuses_shapes_that_do_not_fit():
     """More tokens than one tile, or more workgroups than compute units: an
     error, and the output is left untouched."""
