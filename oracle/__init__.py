@@ -57,6 +57,7 @@ def _load():
         lib.orc_rope_f32.argtypes = [I64, I64, I64, I64, P, P, P, INT]
         lib.orc_block_quant_rows.argtypes = [I64, I64, I64, INT, P, P, P]
         lib.orc_inv_rope_quant.argtypes = [I64, I64, I64, I64, I64, I64, INT, P, P, P, P, P, INT]
+        lib.orc_inv_rope_quant_f32.argtypes = [I64, I64, I64, I64, I64, I64, INT, P, P, P, P, P, INT]
         lib.orc_quant_weight.argtypes = [I64, I64, I64, INT, P, P, P]
         lib.orc_grouped_gemm.argtypes = [I64, I64, I64, I64, P, P, I64, I64, I64, I64, I64, P, P,
                                          I64, P, I64, P, INT]
@@ -66,7 +67,7 @@ def _load():
         lib.orc_e8m0_byte.restype = INT
         lib.orc_e8m0_pack.argtypes = [I64, I64, P, P]
         lib.orc_e8m0_pack.restype = INT
-        for f in (lib.orc_rope_f32, lib.orc_block_quant_rows, lib.orc_inv_rope_quant,
+        for f in (lib.orc_rope_f32, lib.orc_block_quant_rows, lib.orc_inv_rope_quant, lib.orc_inv_rope_quant_f32,
                   lib.orc_quant_weight, lib.orc_grouped_gemm, lib.orc_dense_gemm_bf16,
                   lib.orc_inv_rope_bf16):
             f.restype = None
@@ -174,6 +175,27 @@ def inv_rope_quant(o_bf16, positions, table, n_groups: int, heads_per_group: int
     _load().orc_inv_rope_quant(T, n_groups, heads_per_group, nope_dim, rope_dim, block, int(pow2),
                                _p(o), _p(pos), _p(tab), _p(q), _p(s),
                                nthreads or default_threads())
+    return q, s
+
+
+def inv_rope_quant_f32(o_f32, positions, table, n_groups: int, heads_per_group: int,
+                       nope_dim: int = 448, rope_dim: int = 64, block: int = 128, pow2: bool = False,
+                       nthreads: int | None = None):
+    """The attention-epilogue producer (R11): fp32 o[T, H, head_dim] -> codes
+    [T, G, D], scales [T, G, D/block], the same steps as inv_rope_quant."""
+    o = np.ascontiguousarray(o_f32)
+    assert o.dtype == np.float32
+    pos = _c(positions, np.int64)
+    tab = _c(table, np.float32)
+    T, H, hd = o.shape
+    assert H == n_groups * heads_per_group and hd == nope_dim + rope_dim
+    assert np.all((pos >= 0) & (pos < tab.shape[0]))
+    D = heads_per_group * hd
+    q = np.empty((T, n_groups, D), np.uint8)
+    s = np.empty((T, n_groups, D // block), np.float32)
+    _load().orc_inv_rope_quant_f32(T, n_groups, heads_per_group, nope_dim, rope_dim, block, int(pow2),
+                                   _p(o), _p(pos), _p(tab), _p(q), _p(s),
+                                   nthreads or default_threads())
     return q, s
 
 

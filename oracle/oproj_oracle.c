@@ -48,6 +48,12 @@
  *      blocks, MN-major): the byte of a power-of-two scale 2^k is k + 127 (an
  *      unsigned biased exponent, no mantissa); NaN is 0xFF; block 4j+b of the
  *      row sits in bits 8b..8b+7 of word j (the four bytes in memory order).
+ *  R11 attention-epilogue producer ([OPROJ] rope_quant_attn_out: the output
+ *      pair a fused attention epilogue writes, FP8 codes plus packed UE8M0
+ *      scales, with no bf16 attention output in between): its input is the
+ *      attention output as fp32 values, which go through the same rotation
+ *      (R1, R2) and quantisation (R3-R6) with no rounding to bf16 anywhere.
+ *      For fp32 inputs that are bf16 values it is step a1 + a2 exactly.
  */
 #include <math.h>
 #include <pthread.h>
@@ -246,7 +252,8 @@ void orc_block_quant_rows(int64_t rows, int64_t D, int64_t blk, int pow2, const 
 struct orc_irq_job {
     int64_t t0, t1, G, hpg, nope, rope, blk;
     int pow2;
-    const uint16_t* o;
+    const uint16_t* o; /* bf16 input, or NULL when of is given */
+    const float* of;   /* fp32 input (R11) */
     const int64_t* pos;
     const float* table;
     uint8_t* q;
@@ -265,9 +272,9 @@ static void* orc_irq_worker(void* arg) {
         for (int64_t g = 0; g < j->G; ++g) {
             /* gather the group's heads as fp32, rotating each head's tail */
             for (int64_t hh = 0; hh < j->hpg; ++hh) {
-                const uint16_t* src = j->o + (t * H + g * j->hpg + hh) * hd;
+                const int64_t at = (t * H + g * j->hpg + hh) * hd;
                 float* dst = row + hh * hd;
-                for (int64_t k = 0; k < hd; ++k) dst[k] = orc_bf16_to_f32(src[k]);
+                for (int64_t k = 0; k < hd; ++k) dst[k] = j->of ? j->of[at + k] : orc_bf16_to_f32(j->o[at + k]);
                 orc_inv_rope_row(dst, j->nope, j->rope, trow);
             }
             uint8_t* qd = j->q + (t * j->G + g) * D;
@@ -287,18 +294,31 @@ static int orc_clamp_threads(int64_t n, int nthreads) {
     return nthreads;
 }
 
-void orc_inv_rope_quant(int64_t T, int64_t G, int64_t hpg, int64_t nope, int64_t rope,
-                        int64_t blk, int pow2, const uint16_t* o, const int64_t* pos,
+static void orc_irq_run(int64_t T, int64_t G, int64_t hpg, int64_t nope, int64_t rope, int64_t blk,
+                        int pow2, const uint16_t* o, const float* of, const int64_t* pos,
                         const float* table, uint8_t* q, float* s, int nthreads) {
     nthreads = orc_clamp_threads(T, nthreads);
     pthread_t th[256];
     struct orc_irq_job jobs[256];
     for (int i = 0; i < nthreads; ++i) {
         jobs[i] = (struct orc_irq_job){T * i / nthreads, T * (i + 1) / nthreads, G, hpg, nope, rope,
-                                       blk, pow2, o, pos, table, q, s};
+                                       blk, pow2, o, of, pos, table, q, s};
         pthread_create(&th[i], NULL, orc_irq_worker, &jobs[i]);
     }
     for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
+void orc_inv_rope_quant(int64_t T, int64_t G, int64_t hpg, int64_t nope, int64_t rope,
+                        int64_t blk, int pow2, const uint16_t* o, const int64_t* pos,
+                        const float* table, uint8_t* q, float* s, int nthreads) {
+    orc_irq_run(T, G, hpg, nope, rope, blk, pow2, o, NULL, pos, table, q, s, nthreads);
+}
+
+/* The attention-epilogue producer (R11): the same steps from fp32 o[T][H][head_dim]. */
+void orc_inv_rope_quant_f32(int64_t T, int64_t G, int64_t hpg, int64_t nope, int64_t rope,
+                            int64_t blk, int pow2, const float* o, const int64_t* pos,
+                            const float* table, uint8_t* q, float* s, int nthreads) {
+    orc_irq_run(T, G, hpg, nope, rope, blk, pow2, NULL, o, pos, table, q, s, nthreads);
 }
 
 /* Unquantised step a1 (R1, R2, R9): o[T][H][head_dim] bf16 -> x bf16 in the

@@ -395,6 +395,75 @@ def test_inv_rope_quant_matches_composition():
     assert np.array_equal(q0.reshape(-1, w.D), q3)
 
 
+# ---------------------------------------------------------------- attention-epilogue producer (fp32 input)
+def _f32_attn_out(T, H, seed):
+    """fp32 attention output whose values are not bf16 values (low mantissa bits set)."""
+    x = wl.normal(seed, T * H * 512).astype(np.float32).reshape(T, H, 512)
+    assert np.any(wl.f32_to_bf16_bits(x).astype(np.uint32) << 16 != x.view(np.uint32))
+    return x
+
+
+def test_f32_producer_equals_the_bf16_path_on_bf16_values():
+    """fp32 inputs that are exactly bf16 values give the a1+a2 result bit for bit."""
+    w = wl.WORKLOADS["tiny"]
+    o = wl.attn_out(w)
+    pos, tab = wl.positions(w), wl.table(w)
+    for pow2 in (False, True):
+        q, s = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=pow2)
+        qf, sf = oracle.inv_rope_quant_f32(wl.bf16_bits_to_f32(o), pos, tab, w.n_groups, w.heads_per_group,
+                                           pow2=pow2)
+        assert np.array_equal(q, qf) and np.array_equal(s.view(np.uint32), sf.view(np.uint32))
+
+
+def _torch_encode(v: np.ndarray) -> np.ndarray:
+    """Library route: torch's float8_e4m3fn cast (nearest even) after clamping to +-448."""
+    t = torch.from_numpy(np.clip(v, -448.0, 448.0).astype(np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def test_f32_producer_unrotated_blocks_are_plain_quantisation():
+    """Blocks 0-2 of every head never see the rotation, and at position 0 none
+    does (cos 1, sin 0): there each scale is max|x|/448 of the fp32 input block
+    and each code is the e4m3fn value of x / scale (torch's codec)."""
+    T, G, hpg = 5, 3, 2
+    x = _f32_attn_out(T, G * hpg, 611)
+    tab = wl.cos_sin_table(4096, 64)
+    pos = np.array([0, 17, 4095, 1000, 0], np.int64)
+    q, s = oracle.inv_rope_quant_f32(x, pos, tab, G, hpg)
+    xb = x.reshape(T, G, hpg * 4, 128)          # [t, g, block, 128]
+    sb = s.reshape(T, G, hpg * 4)
+    qb = q.reshape(T, G, hpg * 4, 128)
+    amax = np.abs(xb).max(axis=-1)
+    want_s = (amax / np.float32(448.0)).astype(np.float32)
+    plain = np.zeros((T, G, hpg * 4), bool)
+    plain[:, :, [b for b in range(hpg * 4) if b % 4 != 3]] = True
+    plain[pos == 0] = True
+    assert np.array_equal(sb[plain].view(np.uint32), want_s[plain].view(np.uint32))
+    want_q = _torch_encode(xb / sb[..., None])
+    assert np.array_equal(qb[plain], want_q[plain])
+
+
+def test_f32_producer_rotated_block_scale_within_the_fp64_bound():
+    """Block 3 of each head (64 plain dims + the 32 rotated pairs): its scale is
+    max|v|/448 of the exact (fp64) inverse rotation within the fp32 rounding of
+    the rotation (|error| <= 2^-22 |v| per value) and of the division."""
+    T, G, hpg = 4, 2, 4
+    x = _f32_attn_out(T, G * hpg, 612)
+    tab = wl.cos_sin_table(32768, 64)
+    pos = np.array([3, 32767, 12345, 777], np.int64)
+    _, s = oracle.inv_rope_quant_f32(x, pos, tab, G, hpg)
+    c = tab[pos, :32].astype(np.float64)[:, None, :]
+    sn = tab[pos, 32:].astype(np.float64)[:, None, :]
+    e = x[:, :, 448::2].astype(np.float64)
+    d = x[:, :, 449::2].astype(np.float64)
+    er, dr = e * c + d * sn, d * c - e * sn    # rotation by -theta, pair (e, d)
+    amax = np.maximum(np.abs(x[:, :, 384:448]).max(axis=-1),
+                      np.maximum(np.abs(er).max(axis=-1), np.abs(dr).max(axis=-1)))
+    want = (amax / 448.0).reshape(T, G, hpg)
+    got = s.reshape(T, G, hpg, 4)[..., 3].astype(np.float64)
+    assert np.all(np.abs(got - want) <= want * 2.0 ** -21)
+
+
 # ---------------------------------------------------------------- weights
 def test_weight_quant_and_dequant_blocks():
     rng = np.random.default_rng(12)
