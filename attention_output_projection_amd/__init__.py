@@ -34,6 +34,7 @@ from ._native import (  # noqa: F401
     oproj_grouped_wo_a_bf16,
     oproj_inv_rope_bf16,
     oproj_inv_rope_quant,
+    oproj_inv_rope_quant_f32,
     oproj_quantize_weight,
     oproj_status_string,
     oproj_version,

@@ -124,6 +124,7 @@ def load_library():
             "oproj_fused_bf16_workspace_bytes": (SZ, [SP, I64]),
             "oproj_fused_bf16": (I32, [SP, P, P, P, P, P, I64, P, SZ, P, P]),
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
+            "oproj_inv_rope_quant_f32": (I32, [SP, I32, P, P, P, P, P, LP, P]),
             "oproj_fused_decode": (I32, [SP, I32, P, P, P, P, P, I32, P, SZ, P, P]),
             "oproj_fused_decode_unsupported": (ctypes.c_char_p, [SP, I32, I32]),
             "oproj_quantize_weight": (I32, [I64, I64, I32, I32, P, P, P, P]),
@@ -182,6 +183,14 @@ def oproj_inv_rope_quant(shape: Shape, scale_mode: int, o, positions, cos_sin, a
         ctypes.byref(shape._c()), scale_mode, _ptr(o), _ptr(positions), _ptr(cos_sin),
         _ptr(a_codes), _ptr(a_scales), _lay(out_layout), _stream(stream))
     _check("oproj_inv_rope_quant", st)
+
+
+def oproj_inv_rope_quant_f32(shape: Shape, scale_mode: int, o, positions, cos_sin, a_codes, a_scales,
+                             out_layout: ActLayout | None = None, stream=None) -> None:
+    st = load_library().oproj_inv_rope_quant_f32(
+        ctypes.byref(shape._c()), scale_mode, _ptr(o), _ptr(positions), _ptr(cos_sin),
+        _ptr(a_codes), _ptr(a_scales), _lay(out_layout), _stream(stream))
+    _check("oproj_inv_rope_quant_f32", st)
 
 
 def oproj_grouped_wo_a(shape: Shape, scale_mode: int, a_codes, a_scales, a_layout, w_codes, w_scales,

@@ -119,6 +119,7 @@ oproj_status prep_quant(const oproj_shape* shape, int32_t scale_mode, const void
     a->pow2 = scale_mode != OPROJ_SCALE_FP32;
     a->e8m0 = scale_mode == OPROJ_SCALE_E8M0;
     a->o = static_cast<const uint16_t*>(o);
+    a->o_f32 = nullptr;
     a->positions = positions;
     a->cos_sin = cos_sin;
     a->codes = static_cast<uint8_t*>(a_codes);
@@ -176,6 +177,17 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
     oproj::RopeQuantArgs a;
     const oproj_status st = prep_quant(shape, scale_mode, o, positions, cos_sin, a_codes, a_scales, out_layout, &a);
     if (st != OPROJ_OK || shape->T == 0) return st;
+    return from_hip(oproj::launch_inv_rope_quant(a, static_cast<hipStream_t>(stream)));
+}
+
+oproj_status oproj_inv_rope_quant_f32(const oproj_shape* shape, int32_t scale_mode, const float* o,
+                                     const int64_t* positions, const float* cos_sin, void* a_codes,
+                                     void* a_scales, const oproj_act_layout* out_layout, void* stream) {
+    oproj::RopeQuantArgs a;
+    const oproj_status st = prep_quant(shape, scale_mode, o, positions, cos_sin, a_codes, a_scales, out_layout, &a);
+    if (st != OPROJ_OK || shape->T == 0) return st;
+    a.o = nullptr;
+    a.o_f32 = o;
     return from_hip(oproj::launch_inv_rope_quant(a, static_cast<hipStream_t>(stream)));
 }
 

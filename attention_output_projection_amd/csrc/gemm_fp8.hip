@@ -473,7 +473,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
             const int64_t items = q.T * q.nchunk;
             for (int64_t it = first; it < items; it += step) {
                 const int64_t t = it / q.nchunk, chunk = it % q.nchunk;
-                uint4 raw[QCH];
+                typename rq::Wave<QCH>::RowsT raw;
                 qwv.load_rows(t, g, chunk, raw);
                 const int64_t ps = q.pos[t];
                 float4 cs, sn;

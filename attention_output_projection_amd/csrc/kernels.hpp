@@ -17,6 +17,7 @@ struct RopeQuantArgs {
     int pow2;
     int e8m0;                 // write packed UE8M0 words (one per head: 4 blocks) instead of fp32
     const uint16_t* o;        // bf16 [T][G*hpg][512]
+    const float* o_f32;       // or fp32 [T][G*hpg][512] (then o is unused)
     const int64_t* positions; // [T]
     const float* cos_sin;     // [max_pos][64]
     uint8_t* codes;

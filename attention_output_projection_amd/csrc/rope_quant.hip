@@ -43,18 +43,18 @@ constexpr int kWaves = 4;  // waves per workgroup
 
 typedef rq::Params RQParams;
 
-template <int CH, bool PIPE>
+template <int CH, bool PIPE, bool F32>
 __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWaves;
     const int64_t first = (int64_t)blockIdx.x * kWaves + wave;  // this wave's item k is first + k*nwaves
     if (first >= p.nitems) return;
-    const rq::Wave<CH> w(p, lane);
+    const rq::Wave<CH, F32> w(p, lane);
 
     int64_t tn, gn, cn;
     w.split(first, tn, gn, cn);
-    uint4 rawn[CH];
+    typename rq::Wave<CH, F32>::RowsT rawn;
     w.load_rows(tn, gn, cn, rawn);
     int64_t psn = p.pos[tn];
     float4 csn, snn;
@@ -72,9 +72,7 @@ __global__ __launch_bounds__(kWaves * 64) void inv_rope_quant_kernel(RQParams p)
 
     for (int64_t item = first; item < p.nitems; item += nwaves) {
         const int64_t t = tn, g = gn, chunk = cn, ps = psn;
-        uint4 raw[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) raw[j] = rawn[j];
+        const typename rq::Wave<CH, F32>::RowsT raw = rawn;
         const float4 cs = csn, sn = snn;
         // prefetch item + nwaves (its position is already here) and the
         // position of item + 2*nwaves
@@ -151,11 +149,19 @@ hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kWaves * 64);
     const bool pipe = p.nitems > waves;  // else every wave takes exactly one item
-#define OPROJ_RQ_LAUNCH(C)                                                                    \
-    if (pipe)                                                                                 \
-        hipLaunchKernelGGL((inv_rope_quant_kernel<C, true>), grid, block, 0, stream, p);      \
-    else                                                                                      \
-        hipLaunchKernelGGL((inv_rope_quant_kernel<C, false>), grid, block, 0, stream, p);
+    const bool f32 = a.o_f32 != nullptr;
+#define OPROJ_RQ_LAUNCH(C)                                                                          \
+    if (f32) {                                                                                      \
+        if (pipe)                                                                                   \
+            hipLaunchKernelGGL((inv_rope_quant_kernel<C, true, true>), grid, block, 0, stream, p);  \
+        else                                                                                        \
+            hipLaunchKernelGGL((inv_rope_quant_kernel<C, false, true>), grid, block, 0, stream, p); \
+    } else {                                                                                        \
+        if (pipe)                                                                                   \
+            hipLaunchKernelGGL((inv_rope_quant_kernel<C, true, false>), grid, block, 0, stream, p); \
+        else                                                                                        \
+            hipLaunchKernelGGL((inv_rope_quant_kernel<C, false, false>), grid, block, 0, stream, p);\
+    }
     switch (ch) {
         case 1: OPROJ_RQ_LAUNCH(1) break;
         case 2: OPROJ_RQ_LAUNCH(2) break;

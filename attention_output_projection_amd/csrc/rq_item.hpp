@@ -15,7 +15,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct Params {
-    const uint16_t* o;
+    const uint16_t* o;   // bf16 input rows
+    const float* of;     // or fp32 input rows (the attention-epilogue producer)
     const int64_t* pos;
     const float* table;
     uint8_t* codes;
@@ -32,6 +33,7 @@ inline int heads_per_item(int64_t hpg) { return (hpg % 4 == 0) ? 4 : (int)hpg; }
 inline Params make_params(const RopeQuantArgs& a, int ch) {
     Params p;
     p.o = a.o;
+    p.of = a.o_f32;
     p.pos = a.positions;
     p.table = a.cos_sin;
     p.codes = a.codes;
@@ -52,11 +54,42 @@ inline Params make_params(const RopeQuantArgs& a, int ch) {
     return p;
 }
 
+// The CH head rows of one item as loaded: one 16-byte piece per head and
+// lane for bf16 input, two for fp32 input (lane l: elements 8l..8l+7).
+template <int CH, bool F32>
+struct Rows;
+template <int CH>
+struct Rows<CH, false> {
+    uint4 r[CH];
+    __device__ __forceinline__ void unpack(float (&v)[CH][8]) const {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const uint32_t w4[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                v[j][2 * m] = bf16_lo(w4[m]);
+                v[j][2 * m + 1] = bf16_hi(w4[m]);
+            }
+        }
+    }
+};
+template <int CH>
+struct Rows<CH, true> {
+    u32x4 r[CH][2];
+    __device__ __forceinline__ void unpack(float (&v)[CH][8]) const {
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) v[j][m] = __uint_as_float(r[j][m >> 2][m & 3]);
+    }
+};
+
 // Items are numbered in address order: head chunk fastest, then group, then
 // token.  Lane l holds elements 8l..8l+7 of every head of the chunk, so the
 // 16-lane row c covers quantisation block c and lanes 56..63 the RoPE dims.
-template <int CH>
+template <int CH, bool F32 = false>
 struct Wave {
+    using RowsT = Rows<CH, F32>;
     const Params& p;
     const int lane, c, li;
     const int64_t G;
@@ -73,13 +106,24 @@ struct Wave {
         g = rest % G;
         t = rest / G;
     }
-    // the CH head rows, one 16-byte non-temporal load per head and lane
-    __device__ __forceinline__ void load_rows(int64_t t, int64_t g, int64_t chunk, uint4* raw) const {
-        const uint16_t* src = p.o + (t * p.H + g * p.hpg + chunk * CH) * 512 + 8 * lane;
+    // the CH head rows, non-temporal 16-byte loads (one per head and lane for
+    // bf16, two for fp32)
+    __device__ __forceinline__ void load_rows(int64_t t, int64_t g, int64_t chunk, RowsT& raw) const {
+        const int64_t at = (t * p.H + g * p.hpg + chunk * CH) * 512 + 8 * lane;
+        if constexpr (F32) {
+            const float* src = p.of + at;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
-            raw[j] = make_uint4(x.x, x.y, x.z, x.w);
+            for (int j = 0; j < CH; ++j) {
+                raw.r[j][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
+                raw.r[j][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512 + 4));
+            }
+        } else {
+            const uint16_t* src = p.o + at;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
+                raw.r[j] = make_uint4(x.x, x.y, x.z, x.w);
+            }
         }
     }
     // cos/sin of the lane's 4 pairs (identity for other lanes and bad positions)
@@ -97,22 +141,14 @@ struct Wave {
     // system-scope coherence (written through to memory, for readers in other
     // workgroups of the same launch), else non-temporal codes
     template <bool SYS = false>
-    __device__ __forceinline__ void process(int64_t t, int64_t g, int64_t chunk, int64_t ps, const uint4* raw,
+    __device__ __forceinline__ void process(int64_t t, int64_t g, int64_t chunk, int64_t ps, const RowsT& raw,
                                             float4 cs, float4 sn) const {
         const bool bad = (ps < 0) | (ps >= p.max_pos);
 
         // ---- unpack, rotate the RoPE lanes, per-lane |v| max
         float v[CH][8];
         float am[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const uint32_t w4[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                v[j][2 * m] = bf16_lo(w4[m]);
-                v[j][2 * m + 1] = bf16_hi(w4[m]);
-            }
-        }
+        raw.unpack(v);
         if (lane >= 56) {
             const float cc[4] = {cs.x, cs.y, cs.z, cs.w};
             const float ss[4] = {sn.x, sn.y, sn.z, sn.w};

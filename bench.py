@@ -238,6 +238,79 @@ def bench_bf16(args, w, torch, ap, wl, dev) -> int:
     return 0
 
 
+def bench_epilogue(args, w, torch, ap, wl, dev) -> int:
+    """The attention-epilogue producer alone (oproj_inv_rope_quant_f32: inverse
+    RoPE + FP8 quantisation from fp32 attention output), timed like the path."""
+    if w.prequantised:
+        log("the pre-quantised workload has no attention output")
+        return 2
+    T, H, G = w.T, w.H, w.n_groups
+    log(f"epilogue producer, workload {w.name}: T={T} H={H} G={G} D={w.D}")
+    x = wl.normal_f32_bulk(wl.seed_of(900, 1), T * H * 512).reshape(T, H, 512)
+    pos, tab = wl.positions(w), wl.table(w)
+    copies = args.copies or max(2, min(16, int(np.ceil(768e6 / x.nbytes))))
+    log(f"{copies} rotating copies of {x.nbytes / 1e6:.1f} MB")
+    shp = ap.Shape(T=T, n_groups=G, heads_per_group=w.heads_per_group, o_lora_rank=w.o_lora_rank,
+                   max_pos=w.max_pos)
+    d_pos = torch.from_numpy(pos).to(dev)
+    d_tab = torch.from_numpy(tab).to(dev)
+    C = []
+    for _ in range(copies):
+        C.append({"x": torch.from_numpy(x).to(dev),
+                  "codes": torch.empty((G, T, w.D), dtype=torch.uint8, device=dev),
+                  "scales": torch.empty((G, w.KB, T), dtype=torch.float32, device=dev)})
+    del x
+    torch.cuda.synchronize()
+
+    def run(c):
+        ap.oproj_inv_rope_quant_f32(shp, 0, c["x"], d_pos, d_tab, c["codes"], c["scales"])
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in C:
+            run(c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for c in C:
+            run(c)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // copies)
+    K = reps * copies
+    for _ in range(max(1, args.warmup // copies)):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms_host = (time.perf_counter() - t0) * 1e3 / K
+    us = a.elapsed_time(b) * 1e3 / K
+    nb = T * H * 512 * 4 + T * G * w.D + T * G * w.KB * 4 + T * 8 + T * 64 * 4
+    log(f"{K} launches: {ms_host * 1e3:.2f} us each (host clock), {us:.2f} us (events)")
+    result = {
+        "metric": "tokens/s of the attention-epilogue producer (fp32 in: inverse RoPE + FP8 quant)",
+        "value": T / (ms_host * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": max(1, args.warmup // copies) * copies, "ms_per_step": ms_host,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32->fp8e4m3",
+        "data": "synthetic (seeded SplitMix64 normals)",
+        "config": {"workload": f"{w.name} epilogue producer: T={T} heads={H} n_groups={G} D={w.D}",
+                   "global_batch": T, "parallelism": "single GPU", "copies_rotated": copies},
+        "roofline": {"bound": "hbm", "kernel": "inv_rope_quant_f32", "achieved": nb / (us * 1e3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": nb / (us * 1e3) / HBM_PEAK_GBS,
+                     "traffic": None},
+        "cpu_baseline": None,
+        "kernels": {"inv_rope_quant_f32": {"us": us, "bound": "hbm", "bytes": nb, "GB/s": nb / (us * 1e3)}},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap_ = argparse.ArgumentParser()
     ap_.add_argument("--gpus", type=int, default=1)
@@ -250,9 +323,10 @@ def main() -> int:
                      help="individually timed graph replays for the p10/p50/p90 figures")
     ap_.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
     ap_.add_argument("--no-cpu-baseline", action="store_true")
-    ap_.add_argument("--path", default="fp8", choices=["fp8", "bf16", "one-launch"],
+    ap_.add_argument("--path", default="fp8", choices=["fp8", "bf16", "one-launch", "epilogue"],
                      help="fp8: the quantised path (default); bf16: the unquantised variant; one-launch: "
-                          "the quantised path as one kernel (oproj_fused_decode; decode-sized batches)")
+                          "the quantised path as one kernel (oproj_fused_decode; decode-sized batches); "
+                          "epilogue: the fp32-input producer oproj_inv_rope_quant_f32 alone")
     ap_.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                      help="only run plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap_.parse_args()
@@ -277,6 +351,8 @@ def main() -> int:
     w = wl.WORKLOADS[args.workload]
     if args.path == "bf16":
         return bench_bf16(args, w, torch, ap, wl, dev)
+    if args.path == "epilogue":
+        return bench_epilogue(args, w, torch, ap, wl, dev)
     log(f"workload {w.name}: T={w.T} G={w.n_groups} hpg={w.heads_per_group} D={w.D} R={w.o_lora_rank}")
     one_launch = args.path == "one-launch"
     if one_launch and (w.T > 64 or w.hidden):

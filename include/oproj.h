@@ -137,6 +137,22 @@ oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, 
                                   void* a_scales, const oproj_act_layout* out_layout,
                                   void* stream);
 
+/* The attention-epilogue producer: steps a1 + a2 from the attention output as
+ * fp32 values, the form an attention kernel holds before rounding it to bf16
+ * ([OPROJ] rope_quant_attn_out: the FP8 codes and packed UE8M0 scales a fused
+ * attention epilogue writes instead of a bf16 output; [FUSED] for the steps).
+ * The rotation and quantisation are those of oproj_inv_rope_quant, applied to
+ * the fp32 values with no rounding to bf16 anywhere; for inputs that are bf16
+ * values the results are bit-identical to oproj_inv_rope_quant's.  The same
+ * per-wave work item is what an attention kernel's epilogue would run on its
+ * accumulators; here it reads o from memory so that it can be used and
+ * checked on its own.
+ *  o          fp32 [T][H][512], contiguous, 16-byte aligned
+ * Every other argument, layout, mode and error as for oproj_inv_rope_quant. */
+oproj_status oproj_inv_rope_quant_f32(const oproj_shape* shape, int32_t scale_mode, const float* o,
+                                      const int64_t* positions, const float* cos_sin, void* a_codes,
+                                      void* a_scales, const oproj_act_layout* out_layout, void* stream);
+
 /* Step a3 ([OPROJ] deep_gemm_fp8_o_proj's einsum "bhr,hdr->bhd"; [GWA]):
  *   z[t][g][n] = sum_k (decode(a[t,g,k]) * sa[t,g,k/128])
  *                      * (decode(w[g*R+n][k]) * sw(g*R+n, k/128))

@@ -211,6 +211,18 @@ def test_fused_decode_validation(lib):
     assert dec(shp, mode=0, wblock=2) == E_MODE
 
 
+def test_inv_rope_quant_f32_validation(lib):
+    shp = _shape(T=4, n_groups=2, heads_per_group=2)
+    P = 0x1000
+    f = lambda shape, mode=0, o=P, c=P, s=P: _raw("oproj_inv_rope_quant_f32", ctypes.byref(shape._c()), mode,
+                                                   o, P, P, c, s, None, None)
+    assert f(_shape(T=0), o=None, c=None, s=None) == E_OK
+    assert f(shp, o=None) == E_NULL
+    assert f(shp, o=BAD) == E_ALIGN
+    assert f(shp, mode=3) == E_MODE
+    assert f(_shape(T=4, n_groups=2, heads_per_group=3)) == E_MODE
+
+
 def test_fused_decode_unsupported_reasons(lib):
     """The eligibility query's static reasons (no device needed for these)."""
     q = ap.oproj_fused_decode_unsupported
