@@ -37,6 +37,8 @@
 // the decode kernel's grid with the quantisation (steps a1 + a2) in front:
 // each workgroup quantises its share of its group into a workspace, the
 // group's workgroups meet at a barrier of their own, then each runs its tile.
+#include <cstdlib>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -65,6 +67,7 @@ struct GParams {
     int we8;      // weight scales are packed UE8M0 words (block scaled MFMA only)
     int kshift;   // activation scale words hold 1 << kshift K-blocks (0: fp32, 2: packed UE8M0)
     int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
+    int spin = 0;  // one-launch path: polls of a group barrier before the fallback
 };
 
 // Exponent byte (E8M0) of activation scale word `raw` for K-block kb: the
@@ -342,7 +345,7 @@ __device__ __forceinline__ uint64_t xcc_id() { return __builtin_amdgcn_s_getreg(
 // others.  Returns 0 when every workgroup of the group arrived and all ran on
 // one XCD, 1 when they arrived from several XCDs, 2 when the wait gave up
 // (the caller then does the missing work itself).  Called by one thread.
-__device__ int group_barrier(int64_t g, int64_t n) {
+__device__ int group_barrier(int64_t g, int64_t n, int spin) {
     uint64_t* word = &g_group_sync[kSyncStride * g];
     const uint64_t x = xcc_id();
     const uint64_t inc = 1ull + (x << kSyncSum) + ((x * x) << kSyncSq);
@@ -357,7 +360,7 @@ __device__ int group_barrier(int64_t g, int64_t n) {
         __hip_atomic_fetch_add(word, next - fin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return (int)mixed;
     }
-    for (int it = 0; it < kGroupSpinLimit; ++it) {
+    for (int it = 0; it < spin; ++it) {
         const uint64_t w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((w >> kSyncEpoch) != epoch) return (int)((w >> kSyncMixed) & 1);
         __builtin_amdgcn_s_sleep(2);
@@ -487,7 +490,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         quantise(nt * 8 + (tid >> 6), p.ntiles * 8);
         __shared__ int sync_state;
         __syncthreads();
-        if (tid == 0) sync_state = group_barrier(g, p.ntiles);
+        if (tid == 0) sync_state = group_barrier(g, p.ntiles, p.spin);
         __syncthreads();
         if (sync_state == 2) {
             // a workgroup of the group did not arrive in time: quantise the
@@ -681,6 +684,14 @@ hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a
     p.kbw = a.w_e8m0 ? KB / 4 : KB;
     p.mtiles = 1;
     p.ntiles = ntiles;
+    // OPROJ_FUSED_DECODE_SPIN_LIMIT (diagnostics and tests) lowers the polls a
+    // workgroup makes before it quantises its whole group itself; 0 sends every
+    // workgroup but the last arrival of each group down that fallback
+    p.spin = kGroupSpinLimit;
+    if (const char* e = getenv("OPROJ_FUSED_DECODE_SPIN_LIMIT")) {
+        const long v = strtol(e, nullptr, 10);
+        p.spin = v < 0 ? 0 : (v < kGroupSpinLimit ? (int)v : kGroupSpinLimit);
+    }
     const rq::Params q = rq::make_params(qa, ch);
     const dim3 grid((unsigned)(a.G * ntiles)), block(DKS * 256);
 #define OPROJ_FUSED_LAUNCH(MXV, W1V, CHV) \

@@ -267,7 +267,9 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
  * Concurrency: calls on one device must not overlap in time, on any streams:
  * they share the library's per-group barrier words on that device.  A
  * workgroup that waits too long at its barrier quantises its whole group
- * itself, so a slow neighbour costs time, never correctness. */
+ * itself, so a slow neighbour costs time, never correctness.  The environment
+ * variable OPROJ_FUSED_DECODE_SPIN_LIMIT (read at each call; diagnostics and
+ * tests) lowers the number of polls before that fallback, down to 0. */
 oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, const void* o,
                                 const int64_t* positions, const float* cos_sin, const void* w_codes,
                                 const void* w_scales, int32_t w_block, void* workspace,

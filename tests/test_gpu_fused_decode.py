@@ -158,6 +158,27 @@ def test_one_launch_back_to_back_changing_group_sizes():
             assert torch.equal(outs[k][i], refs[k]), (k, i)
 
 
+@pytest.mark.parametrize("spin", ["0", "1"])
+def test_one_launch_fallback_path(spin, monkeypatch):
+    """With the barrier's poll limit forced down from the host, every workgroup
+    but a group's last arrival gives up waiting and quantises its whole group
+    itself: the result is still bit-identical to the two-launch path."""
+    c = _Case(445, 64, 16, 8, 1024, P2, B1)
+    ref = c.zbuf()
+    c.two_launch(c.wsbuf(), ref)
+    monkeypatch.setenv("OPROJ_FUSED_DECODE_SPIN_LIMIT", spin)
+    outs = [c.zbuf() for _ in range(3)]
+    ws = c.wsbuf()
+    for z in outs:
+        c.one_launch(ws, z)
+    monkeypatch.delenv("OPROJ_FUSED_DECODE_SPIN_LIMIT")
+    z_after = c.zbuf()
+    c.one_launch(ws, z_after)  # and the barrier words are left in order for normal calls
+    torch.cuda.synchronize()
+    for z in outs + [z_after]:
+        assert torch.equal(z, ref)
+
+
 def test_one_launch_graph_replays():
     """Captured in a HIP graph: every replay, with eager calls of the same
     entry point and new inputs between replays, equals the eager result."""
