@@ -1,8 +1,10 @@
 /*
  * oproj.h -- C ABI of the MI355X (gfx950) O-projection front half:
  *   inverse RoPE -> 1x128 block FP8 e4m3fn quantisation -> grouped wo_a GEMM
- *   [-> dense wo_b GEMM], and the unquantised variant (bf16 inverse RoPE ->
- *   grouped bf16 wo_a GEMM).
+ *   [-> dense wo_b GEMM] (as separate calls, in two launches, or in one launch
+ *   for decode-sized batches), the same rotation and quantisation from fp32
+ *   attention output (the attention-epilogue producer), and the unquantised
+ *   variant (bf16 inverse RoPE -> grouped bf16 wo_a GEMM).
  *
  * Sources (web pages; cited by page title and section):
  *  [FUSED] vLLM API page "vllm.models.deepseek_v4.common.ops.fused_inv_rope_fp8_quant",
