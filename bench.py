@@ -90,20 +90,25 @@ def load_traffic(kernel: str, workload: str, sha: str):
     return int(d["bytes_per_launch"])
 
 
-def cpu_baseline(w, o, pos, tab, wmat, max_tokens: int):
-    """The oracle as it stands, on the first tokens of the same batch."""
+def cpu_baseline(w, o, pos, tab, wmat, max_tokens: int, reps: int = 3):
+    """The oracle as it stands, on the first tokens of the same batch; the
+    median of `reps` runs."""
     import oracle
 
     S = min(w.T, max_tokens)
     qw, sw = oracle.quant_weight(wmat, w.w_block_rows, w.pow2)  # offline weight prep, untimed
     threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    qa, sa = oracle.inv_rope_quant(o[:S], pos[:S], tab, w.n_groups, w.heads_per_group, pow2=w.pow2)
-    oracle.grouped_gemm(qa, sa, qw, sw, w.n_groups, w.o_lora_rank, w.w_block_rows)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        qa, sa = oracle.inv_rope_quant(o[:S], pos[:S], tab, w.n_groups, w.heads_per_group, pow2=w.pow2)
+        oracle.grouped_gemm(qa, sa, qw, sw, w.n_groups, w.o_lora_rank, w.w_block_rows)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     return {"value": S / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of {w.T} tokens of the {w.name} batch: inverse RoPE + quant + "
-                      f"grouped wo_a in fp64, {dt:.2f} s"}
+                      f"grouped wo_a in fp64, median of {reps} runs of {dt:.2f} s "
+                      f"({sum(times):.1f} s of CPU work)"}
 
 
 def copy_calibration(torch, dev, mib: int) -> int:
