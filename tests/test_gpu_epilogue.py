@@ -73,6 +73,24 @@ def test_f32_producer_parity(T, G, hpg, mode):
         U.assert_scales_bitexact(sg, sr)
 
 
+@pytest.mark.parametrize("mode", [0, 2])
+def test_f32_producer_pipelined_launch(mode):
+    """Enough items for the pipelined instance with four-head items and the
+    fixed wave population that bench.py times at prefill (T=2048, 16 x 8
+    heads), checked in full against the oracle."""
+    T, G, hpg = 2048, 16, 8
+    x = wl.normal_f32_bulk(wl.seed_of(750, 1), T * G * hpg * 512).reshape(T, G * hpg, 512)
+    tab = wl.cos_sin_table(32768, 64)
+    pos = wl.uniform_int(wl.seed_of(750, 2), T, 0, 32768).astype(np.int64)
+    qg, sg = gpu_quant_f32(x, pos, tab, G, hpg, mode)
+    qr, sr = oracle.inv_rope_quant_f32(x, pos, tab, G, hpg, pow2=mode != 0)
+    U.assert_codes_parity(qg, qr)
+    if mode == 2:
+        assert np.array_equal(sg.view(np.uint32), oracle.e8m0_pack(sr))
+    else:
+        U.assert_scales_bitexact(sg, sr)
+
+
 def test_f32_producer_equals_bf16_entry_point_on_bf16_values():
     w = wl.WORKLOADS["decode"]
     o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
