@@ -48,6 +48,8 @@
  *      blocks, MN-major): the byte of a power-of-two scale 2^k is k + 127 (an
  *      unsigned biased exponent, no mantissa); NaN is 0xFF; block 4j+b of the
  *      row sits in bits 8b..8b+7 of word j (the four bytes in memory order).
+ *  R2, R3 and R4 are conventions the pages leave open: parity unpinned for
+ *  those choices (both sides follow them; the tests pin everything else).
  *  R11 attention-epilogue producer ([OPROJ] rope_quant_attn_out: the output
  *      pair a fused attention epilogue writes, FP8 codes plus packed UE8M0
  *      scales, with no bf16 attention output in between): its input is the
