@@ -76,11 +76,23 @@ struct Rows<CH, false> {
 template <int CH>
 struct Rows<CH, true> {
     u32x4 r[CH][2];
+    // Loaded contiguously (half the memory requests of two 16-byte pieces per
+    // lane 32 bytes apart): r[j][0] holds floats 4l..4l+3 of head j, r[j][1]
+    // floats 256+4l..256+4l+3; lane l's elements 8l..8l+7 sit in lanes 2l and
+    // 2l+1 (mod 64), in the first load for l < 32 and the second above
     __device__ __forceinline__ void unpack(float (&v)[CH][8]) const {
+        const int l = __lane_id();
+        const int sa = (2 * l) & 63, sb = (2 * l + 1) & 63;
+        const bool up = l >= 32;
 #pragma unroll
         for (int j = 0; j < CH; ++j)
 #pragma unroll
-            for (int m = 0; m < 8; ++m) v[j][m] = __uint_as_float(r[j][m >> 2][m & 3]);
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a0 = __shfl(r[j][0][k], sa), a1 = __shfl(r[j][1][k], sa);
+                const uint32_t b0 = __shfl(r[j][0][k], sb), b1 = __shfl(r[j][1][k], sb);
+                v[j][k] = __uint_as_float(up ? a1 : a0);
+                v[j][4 + k] = __uint_as_float(up ? b1 : b0);
+            }
     }
 };
 
@@ -106,19 +118,20 @@ struct Wave {
         g = rest % G;
         t = rest / G;
     }
-    // the CH head rows, non-temporal 16-byte loads (one per head and lane for
-    // bf16, two for fp32)
+    // the CH head rows, non-temporal 16-byte loads (bf16: one per head and
+    // lane, elements 8l..8l+7; fp32: two per head and lane, each instruction
+    // reading 1 KiB of the row contiguously, rearranged by unpack())
     __device__ __forceinline__ void load_rows(int64_t t, int64_t g, int64_t chunk, RowsT& raw) const {
-        const int64_t at = (t * p.H + g * p.hpg + chunk * CH) * 512 + 8 * lane;
+        const int64_t row0 = (t * p.H + g * p.hpg + chunk * CH) * 512;
         if constexpr (F32) {
-            const float* src = p.of + at;
+            const float* src = p.of + row0 + 4 * lane;
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 raw.r[j][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
-                raw.r[j][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512 + 4));
+                raw.r[j][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512 + 256));
             }
         } else {
-            const uint16_t* src = p.o + at;
+            const uint16_t* src = p.o + row0 + 8 * lane;
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)j * 512));
