@@ -250,3 +250,28 @@ def test_one_launch_refuses_shapes_that_do_not_fit():
     assert ei.value.status == 2
     torch.cuda.synchronize()
     assert bool((z == 0x7BAD).all()) and bool((zw == 0x7BAD).all())
+
+
+def test_two_launch_path_is_safe_on_concurrent_streams():
+    """oproj_fused keeps no state between calls: calls on two streams at once,
+    each with its own workspace, give the single-stream results."""
+    cases = [_Case(470, 64, 16, 8, 1024, F32, B128), _Case(471, 48, 16, 8, 1024, P2, B1)]
+    refs = []
+    for c in cases:
+        z = c.zbuf()
+        c.two_launch(c.wsbuf(), z)
+        refs.append(z)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[c.zbuf() for _ in range(8)] for c in cases]
+    wss = [c.wsbuf() for c in cases]
+    torch.cuda.synchronize()
+    for i in range(8):
+        for k, c in enumerate(cases):
+            with torch.cuda.stream(streams[k]):
+                ap.oproj_fused(c.shp, c.mode, c.d_o, c.d_pos, c.d_tab, c.d_wq, c.d_ws, c.wblock, None, 0,
+                               wss[k], c.nbytes, outs[k][i], stream=streams[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        for i in range(8):
+            assert torch.equal(outs[k][i], refs[k]), (k, i)
