@@ -1,0 +1,114 @@
+"""Tensor-level calls in the shape of the pages' functions, over the C ABI.
+
+vLLM API page "vllm.models.deepseek_v4.common.ops.fused_inv_rope_fp8_quant"
+(fused_inv_rope_fp8_quant: returns o_fp8 [T, G, D] with strides (D, T*D, 1)
+and the MN-major scales) and vLLM API page
+"vllm.models.deepseek_v4.nvidia.ops.o_proj" (deep_gemm_fp8_o_proj: inverse
+RoPE + grouped wo_a + wo_b over the flattened z; a pre-quantised input is
+sliced to its live groups).
+
+Argument marshalling only: these functions allocate the outputs (and the
+workspace) with torch.empty on the input's device, read strides off the
+tensors, and call one entry point of liboproj.so; every arithmetic step runs
+in the HIP kernels.  Differences from the pages: wo_a is passed as its FP8
+codes and scales (as oproj_quantize_weight writes them), wo_b as a bf16
+[hidden, G*R] tensor rather than a module, and the scale recipe as a scale
+mode (OPROJ_SCALE_FP32, OPROJ_SCALE_POW2 or OPROJ_SCALE_E8M0, the last being
+the packed UE8M0 words) instead of (einsum_recipe, tma_aligned_scales); scales
+are not padded to a TMA-aligned token count.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _native as n
+
+
+def _scale_dtype(scale_mode: int):
+    return torch.int32 if scale_mode == n.OPROJ_SCALE_E8M0 else torch.float32
+
+
+def fused_inv_rope_fp8_quant(o: torch.Tensor, positions: torch.Tensor, cos_sin_cache: torch.Tensor,
+                             n_groups: int, heads_per_group: int, nope_dim: int = 448, rope_dim: int = 64,
+                             quant_group_size: int = 128, scale_mode: int = n.OPROJ_SCALE_FP32):
+    """a1 + a2 on bf16 o [T, H, 512] (fp32 o: the attention-epilogue producer).
+
+    Returns (o_fp8, o_scale): o_fp8 is [T, G, D] float8_e4m3fn with strides
+    (D, T*D, 1) over group-major storage; o_scale is [T, G, KB] float32 with
+    strides (1, KB*T, T) over [G, KB, T] storage, or [T, G, KB/4] int32 packed
+    UE8M0 words in OPROJ_SCALE_E8M0 mode."""
+    T, H, hd = o.shape
+    shape = n.Shape(T=T, n_groups=n_groups, heads_per_group=heads_per_group, max_pos=cos_sin_cache.shape[0],
+                    nope_dim=nope_dim, rope_dim=rope_dim, quant_block=quant_group_size)
+    if H != n_groups * heads_per_group or hd != nope_dim + rope_dim:
+        raise ValueError(f"o is [{T}, {H}, {hd}]: expected [T, {n_groups * heads_per_group}, {nope_dim + rope_dim}]")
+    nw = shape.KB // 4 if scale_mode == n.OPROJ_SCALE_E8M0 else shape.KB
+    codes = torch.empty((n_groups, T, shape.D), dtype=torch.float8_e4m3fn, device=o.device)
+    scales = torch.empty((n_groups, nw, T), dtype=_scale_dtype(scale_mode), device=o.device)
+    call = n.oproj_inv_rope_quant_f32 if o.dtype == torch.float32 else n.oproj_inv_rope_quant
+    call(shape, scale_mode, o.contiguous(), positions, cos_sin_cache, codes, scales)
+    return codes.transpose(0, 1), scales.permute(2, 0, 1)
+
+
+def quantize_wo_a(w: torch.Tensor, w_block: int = n.OPROJ_WBLOCK_128x128,
+                  scale_mode: int = n.OPROJ_SCALE_FP32):
+    """Offline: fp32 wo_a [G*R, D] -> (FP8 codes [G*R, D], scales).  Scales are
+    float32 [ceil(rows/128), D/128] (128x128 blocks) or [rows, D/128] (1x128),
+    or int32 [rows, D/512] packed UE8M0 words (OPROJ_WBLOCK_1x128_UE8M0)."""
+    rows, K = w.shape
+    codes = torch.empty((rows, K), dtype=torch.float8_e4m3fn, device=w.device)
+    if w_block == n.OPROJ_WBLOCK_1x128_UE8M0:
+        scales = torch.empty((rows, K // 512), dtype=torch.int32, device=w.device)
+    elif w_block == n.OPROJ_WBLOCK_1x128:
+        scales = torch.empty((rows, K // 128), dtype=torch.float32, device=w.device)
+    else:
+        scales = torch.empty(((rows + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    n.oproj_quantize_weight(rows, K, w_block, scale_mode, w.contiguous(), codes, scales)
+    return codes, scales
+
+
+def grouped_wo_a(o_fp8: torch.Tensor, o_scale: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, *,
+                 n_groups: int, heads_per_group: int, o_lora_rank: int, scale_mode: int = n.OPROJ_SCALE_FP32,
+                 w_block: int = n.OPROJ_WBLOCK_128x128) -> torch.Tensor:
+    """a3 on FP8 activations given as [T, >=G, D] codes and [T, >=G, KB] scales
+    views of any strides (only groups < n_groups are read: a padded
+    pre-quantised input is passed as it is).  Returns z bf16 [T, G, R]."""
+    T = o_fp8.shape[0]
+    shape = n.Shape(T=T, n_groups=n_groups, heads_per_group=heads_per_group, o_lora_rank=o_lora_rank)
+    if o_fp8.shape[2] != shape.D or o_fp8.stride(2) != 1:
+        raise ValueError("o_fp8 must be [T, G, D] with unit stride along D")
+    lay = n.ActLayout(o_fp8.stride(0), o_fp8.stride(1), o_scale.stride(0), o_scale.stride(1), o_scale.stride(2))
+    z = torch.empty((T, n_groups, o_lora_rank), dtype=torch.bfloat16, device=o_fp8.device)
+    n.oproj_grouped_wo_a(shape, scale_mode, o_fp8, o_scale, lay, w_codes, w_scales, w_block, z)
+    return z
+
+
+def deep_gemm_fp8_o_proj(o: torch.Tensor, positions: torch.Tensor, cos_sin_cache: torch.Tensor,
+                         w_codes: torch.Tensor, w_scales: torch.Tensor, wo_b: torch.Tensor | None = None, *,
+                         n_groups: int, heads_per_group: int, o_lora_rank: int,
+                         scale_mode: int = n.OPROJ_SCALE_FP32, w_block: int = n.OPROJ_WBLOCK_128x128,
+                         one_launch: bool = False) -> torch.Tensor:
+    """The whole path on bf16 o [T, H, 512]: y = wo_b(z.flatten(1)) bf16
+    [T, hidden] when wo_b ([hidden, G*R] bf16) is given, else z bf16 [T, G, R].
+    one_launch takes oproj_fused_decode (steps a1-a3 in one kernel) when it
+    supports the shape and wo_b is None, and oproj_fused otherwise."""
+    T = o.shape[0]
+    shape = n.Shape(T=T, n_groups=n_groups, heads_per_group=heads_per_group, o_lora_rank=o_lora_rank,
+                    max_pos=cos_sin_cache.shape[0])
+    hidden = 0 if wo_b is None else wo_b.shape[0]
+    ws_bytes = n.oproj_fused_workspace_bytes(shape, hidden)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
+    o = o.contiguous()
+    if wo_b is None:
+        z = torch.empty((T, n_groups, o_lora_rank), dtype=torch.bfloat16, device=o.device)
+        if one_launch and n.oproj_fused_decode_unsupported(shape, scale_mode, w_block) is None:
+            n.oproj_fused_decode(shape, scale_mode, o, positions, cos_sin_cache, w_codes, w_scales, w_block,
+                                 ws, ws_bytes, z)
+        else:
+            n.oproj_fused(shape, scale_mode, o, positions, cos_sin_cache, w_codes, w_scales, w_block, None, 0,
+                          ws, ws_bytes, z)
+        return z
+    y = torch.empty((T, hidden), dtype=torch.bfloat16, device=o.device)
+    n.oproj_fused(shape, scale_mode, o, positions, cos_sin_cache, w_codes, w_scales, w_block, wo_b.contiguous(),
+                  hidden, ws, ws_bytes, y)
+    return y

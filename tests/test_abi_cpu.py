@@ -257,3 +257,11 @@ def test_binding_raises_on_error_status(lib):
     with pytest.raises(ap.OprojError) as ei:
         ap.oproj_inv_rope_quant(_shape(heads_per_group=3), 0, 1, 1, 1, 1, 1, stream=0)
     assert ei.value.status == E_MODE
+
+
+def test_torch_ops_checks_shapes_before_touching_a_device():
+    import torch
+    from attention_output_projection_amd import torch_ops as to
+    o = torch.zeros((4, 6, 512), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        to.fused_inv_rope_fp8_quant(o, torch.zeros(4, dtype=torch.int64), torch.zeros((16, 64)), 2, 2)
