@@ -168,6 +168,27 @@ oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void*
     return OPROJ_OK;
 }
 
+// Validation and workspace layout shared by the FP8 whole-path entry points:
+// the codes, then the scales, then (when hidden > 0) z, each region 256-byte
+// aligned; a3 writes z there or, without wo_b, straight to out.
+oproj_status prep_fused(const oproj_shape* shape, int32_t scale_mode, const void* o, const int64_t* positions,
+                        const float* cos_sin, const void* w_codes, const void* w_scales, int32_t w_block,
+                        int64_t hidden, void* workspace, size_t workspace_bytes, void* out,
+                        oproj::RopeQuantArgs* qa, oproj::GroupedGemmArgs* ga, void** zbuf) {
+    if (!o || !positions || !cos_sin || !w_codes || !w_scales || !workspace || !out) return OPROJ_E_NULL;
+    if (workspace_bytes < oproj_fused_workspace_bytes(shape, hidden)) return OPROJ_E_SHAPE;
+    if (!aligned16(workspace)) return OPROJ_E_ALIGN;
+    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;
+    const size_t D = (size_t)shape->heads_per_group * 512, KB = D / 128;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* codes = ws;
+    float* scales = reinterpret_cast<float*>(ws + round_up(T * G * D));
+    *zbuf = hidden > 0 ? (void*)(ws + round_up(T * G * D) + round_up(T * G * KB * sizeof(float))) : out;
+    oproj_status st = prep_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, qa);
+    if (st != OPROJ_OK) return st;
+    return prep_gemm(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block, *zbuf, ga);
+}
+
 }  // namespace
 
 oproj_status oproj_inv_rope_quant(const oproj_shape* shape, int32_t scale_mode, const void* o,
@@ -353,22 +374,11 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
     if (!valid_wblock(w_block, scale_mode)) return OPROJ_E_MODE;
     if (wo_b && (hidden < 16 || hidden % 16 != 0)) return OPROJ_E_SHAPE;
     if (shape->T == 0) return OPROJ_OK;
-    if (!o || !positions || !cos_sin || !w_codes || !w_scales || !workspace || !out)
-        return OPROJ_E_NULL;
-    if (workspace_bytes < oproj_fused_workspace_bytes(shape, wo_b ? hidden : 0)) return OPROJ_E_SHAPE;
-    if (!aligned16(workspace)) return OPROJ_E_ALIGN;
-    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups;
-    const size_t D = (size_t)shape->heads_per_group * 512, KB = D / 128;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* codes = ws;
-    float* scales = reinterpret_cast<float*>(ws + round_up(T * G * D));
-    void* zbuf = wo_b ? (void*)(ws + round_up(T * G * D) + round_up(T * G * KB * sizeof(float))) : out;
     oproj::RopeQuantArgs qa;
     oproj::GroupedGemmArgs ga;
-    if ((st = prep_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, &qa)) != OPROJ_OK)
-        return st;
-    if ((st = prep_gemm(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block, zbuf, &ga)) !=
-        OPROJ_OK)
+    void* zbuf = nullptr;
+    if ((st = prep_fused(shape, scale_mode, o, positions, cos_sin, w_codes, w_scales, w_block, wo_b ? hidden : 0,
+                         workspace, workspace_bytes, out, &qa, &ga, &zbuf)) != OPROJ_OK)
         return st;
     if (wo_b) {  // validate a4 before anything is enqueued
         const int64_t K = shape->n_groups * shape->o_lora_rank, lim = int64_t(1) << 32;
@@ -394,19 +404,11 @@ oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, co
     if (shape->T > 64 || shape->n_groups > 256) return OPROJ_E_SHAPE;
     if (shape->heads_per_group != 2 && shape->heads_per_group % 4 != 0) return OPROJ_E_MODE;
     if (shape->T == 0) return OPROJ_OK;
-    if (!o || !positions || !cos_sin || !w_codes || !w_scales || !workspace || !z) return OPROJ_E_NULL;
-    if (workspace_bytes < oproj_fused_workspace_bytes(shape, 0)) return OPROJ_E_SHAPE;
-    if (!aligned16(workspace)) return OPROJ_E_ALIGN;
-    const size_t T = (size_t)shape->T, G = (size_t)shape->n_groups, D = (size_t)shape->heads_per_group * 512;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* codes = ws;
-    float* scales = reinterpret_cast<float*>(ws + round_up(T * G * D));
     oproj::RopeQuantArgs qa;
     oproj::GroupedGemmArgs ga;
-    if ((st = prep_quant(shape, scale_mode, o, positions, cos_sin, codes, scales, nullptr, &qa)) != OPROJ_OK)
-        return st;
-    if ((st = prep_gemm(shape, scale_mode, codes, scales, nullptr, w_codes, w_scales, w_block, z, &ga)) !=
-        OPROJ_OK)
+    void* zbuf = nullptr;
+    if ((st = prep_fused(shape, scale_mode, o, positions, cos_sin, w_codes, w_scales, w_block, 0, workspace,
+                         workspace_bytes, z, &qa, &ga, &zbuf)) != OPROJ_OK)
         return st;
     bool launched = false;
     if ((st = from_hip(oproj::launch_fused_decode(qa, ga, static_cast<hipStream_t>(stream), &launched))) !=
