@@ -308,9 +308,11 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 // one s_waitcnt + barrier per K-block.  In a K-group, waves 0-1 issue the
 // copies (a copy waits at issue while the CU's memory pipeline is full) and
 // waves 2-3 only compute.  Rows are 128 bytes with the 16-byte pieces
-// XOR-swizzled, which makes the fragment reads conflict-free.  For the MFMAs the waves split N (wave w owns columns
-// 16w..16w+15); the K-groups' partial tiles are summed through LDS and
-// written as whole 128-byte rows of z.
+// XOR-swizzled, which makes the fragment reads conflict-free.  For the MFMAs
+// the waves of a K-group split M: wave w owns token rows 16w..16w+15 against
+// all 64 columns (one activation and four weight fragments per K-block, a
+// third less LDS reading than splitting N); the K-groups' partial tiles are
+// summed through LDS and written as whole 128-byte rows of z.
 #ifndef OPROJ_DEC_DNS
 #define OPROJ_DEC_DNS 4
 #endif
@@ -537,34 +539,37 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         if (copier && i + DNS - 1 < nkb) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
         if (i >= nkb) continue;        // uniform per wave group
         const uint8_t* st = ring[kq][i % DNS];
-        v8i bfr;
-        {
-            const int r = 16 * wave + frow;
-            const uint4 lo = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * (p0 ^ swz(r)));
-            const uint4 hi = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
-            bfr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        // wave w: the 16 token rows 16w..16w+15 against all 64 columns (one
+        // activation fragment, four weight fragments per K-block)
         const float* sc = reinterpret_cast<const float*>(st + 16384);
         // scales: [64 * c + t] activation scale of token 32c + t, [64 * c + 32 + j]
         // weight scale of column 32c + j (c = copying wave)
-        const float swv = sc[64 * (wave >> 1) + 32 + 16 * (wave & 1) + (W1 || MX ? frow : 0)];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r = 16 * mi + frow;
+        v8i af;
+        {
+            const int r = 16 * wave + frow;
             const uint4 lo = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * (p0 ^ swz(r)));
             const uint4 hi = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
-            const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        const float* sct = sc + 64 * (wave >> 1) + 16 * (wave & 1);  // this wave's 16 token scales
+        float4 t4;
+        int ea = 0;
+        if constexpr (MX) ea = act_e8m0(p, __float_as_uint(sct[frow]), kb0 + i);
+        else t4 = *reinterpret_cast<const float4*>(sct + 4 * (lane >> 4));
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int r = 16 * ni + frow;
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * (p0 ^ swz(r)));
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
+            const v8i bfr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const float swv = sc[64 * (ni >> 1) + 32 + 16 * (ni & 1) + (W1 || MX ? frow : 0)];
             if constexpr (MX) {
-                const uint32_t raw = __float_as_uint(sc[64 * (mi >> 1) + 16 * (mi & 1) + frow]);
-                acc[mi] = mfma_fp8_mx(af, bfr, acc[mi], act_e8m0(p, raw, kb0 + i),
-                                      w_e8m0(p, __float_as_uint(swv), kb0 + i));
+                acc[ni] = mfma_fp8_mx(af, bfr, acc[ni], ea, w_e8m0(p, __float_as_uint(swv), kb0 + i));
             } else {
-                const float4 t4 =
-                    *reinterpret_cast<const float4*>(&sc[64 * (mi >> 1) + 16 * (mi & 1) + 4 * (lane >> 4)]);
                 const float cmb[4] = {t4.x * swv, t4.y * swv, t4.z * swv, t4.w * swv};
                 const v4f pp = mfma_fp8(af, bfr, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) acc[mi][i2] = __builtin_fmaf(pp[i2], cmb[i2], acc[mi][i2]);
+                for (int i2 = 0; i2 < 4; ++i2) acc[ni][i2] = __builtin_fmaf(pp[i2], cmb[i2], acc[ni][i2]);
             }
         }
     }
@@ -576,10 +581,10 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // and writes it to z as bf16: whole 128-byte tile rows, 16-byte stores
     float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [DKS][64][DPROW]
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            part[(kq * DBM + 16 * mi + 4 * (lane >> 4) + i) * DPROW + 16 * wave + frow] = acc[mi][i];
+            part[(kq * DBM + 16 * wave + 4 * (lane >> 4) + i) * DPROW + 16 * ni + frow] = acc[ni][i];
     __syncthreads();
     for (int idx = tid; idx < DBM * (DBN / 8); idx += DKS * 256) {
         const int r = idx / (DBN / 8), ch = idx % (DBN / 8);
