@@ -215,7 +215,7 @@ __global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[XKS][XNS][XSTAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
-    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row group of the tile
     const bool copier = wave < 2;
     const int64_t per = p.mtiles * p.ntiles;
     const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per);
@@ -270,16 +270,17 @@ __global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) 
         if (copier && i + XNS - 1 < ns) issue(i + XNS - 1, (int)((i + XNS - 1) % XNS));
         if (i >= ns) continue;  // uniform per K-group
         const uint8_t* st = ring[kq][i % XNS];
-        const int rb = 16 * wave + frow;
-        const v8bf blo = *reinterpret_cast<const v8bf*>(st + 8192 + rb * 128 + 16 * (p0 ^ swz(rb)));
-        const v8bf bhi = *reinterpret_cast<const v8bf*>(st + 8192 + rb * 128 + 16 * ((p0 + 1) ^ swz(rb)));
+        // wave w: token rows 16w..16w+15 against all 64 columns
+        const int ra = 16 * wave + frow;
+        const v8bf alo = *reinterpret_cast<const v8bf*>(st + ra * 128 + 16 * (p0 ^ swz(ra)));
+        const v8bf ahi = *reinterpret_cast<const v8bf*>(st + ra * 128 + 16 * ((p0 + 1) ^ swz(ra)));
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r = 16 * mi + frow;
-            const v8bf alo = *reinterpret_cast<const v8bf*>(st + r * 128 + 16 * (p0 ^ swz(r)));
-            const v8bf ahi = *reinterpret_cast<const v8bf*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
-            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo, acc[mi], 0, 0, 0);
-            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[mi], 0, 0, 0);
+        for (int ni = 0; ni < 4; ++ni) {
+            const int r = 16 * ni + frow;
+            const v8bf blo = *reinterpret_cast<const v8bf*>(st + 8192 + r * 128 + 16 * (p0 ^ swz(r)));
+            const v8bf bhi = *reinterpret_cast<const v8bf*>(st + 8192 + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
+            acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, blo, acc[ni], 0, 0, 0);
+            acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[ni], 0, 0, 0);
         }
     }
     wait_vmcnt<0>();  // (already true: the last step was waited for in full)
@@ -287,10 +288,10 @@ __global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) 
 
     float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [XKS][64][XPROW]
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            part[(kq * XBM + 16 * mi + 4 * (lane >> 4) + i) * XPROW + 16 * wave + frow] = acc[mi][i];
+            part[(kq * XBM + 16 * wave + 4 * (lane >> 4) + i) * XPROW + 16 * ni + frow] = acc[ni][i];
     __syncthreads();
     for (int idx = tid; idx < XBM * (XBN / 8); idx += XKS * 256) {
         const int r = idx / (XBN / 8), ch = idx % (XBN / 8);
