@@ -66,6 +66,11 @@ class _Case:
     def wsbuf(self):
         return torch.full((self.nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
 
+    def require_one_launch(self):
+        why = ap.oproj_fused_decode_unsupported(self.shp, self.mode, self.wblock)
+        if why is not None:  # e.g. a partitioned device with fewer compute units
+            pytest.skip(f"one-launch path unavailable here: {why}")
+
     def one_launch(self, ws, z):
         ap.oproj_fused_decode(self.shp, self.mode, self.d_o, self.d_pos, self.d_tab, self.d_wq, self.d_ws,
                               self.wblock, ws, self.nbytes, z)
@@ -106,6 +111,7 @@ CASES = [
 @pytest.mark.parametrize("T,G,hpg,R,mode,wblock", CASES)
 def test_one_launch_equals_two_launches_and_oracle(T, G, hpg, R, mode, wblock):
     c = _Case(400 + T + 7 * G + hpg, T, G, hpg, R, mode, wblock)
+    c.require_one_launch()
     ws1, z1 = c.wsbuf(), c.zbuf()
     c.one_launch(ws1, z1)
     ws2, z2 = c.wsbuf(), c.zbuf()
@@ -125,6 +131,7 @@ def test_one_launch_equals_two_launches_and_oracle(T, G, hpg, R, mode, wblock):
 def test_one_launch_bad_positions():
     """Positions outside the table give NaN scales: same bits as oproj_fused."""
     c = _Case(431, 24, 4, 8, 256, F32, B128, bad_positions=True)
+    c.require_one_launch()
     z1, z2 = c.zbuf(), c.zbuf()
     c.one_launch(c.wsbuf(), z1)
     c.two_launch(c.wsbuf(), z2)
@@ -140,6 +147,8 @@ def test_one_launch_back_to_back_changing_group_sizes():
     16, 4 and 1 workgroups: the barrier words carry over from call to call."""
     cases = [_Case(440, 64, 16, 8, 1024, F32, B128), _Case(441, 9, 6, 4, 256, P2, B1),
              _Case(442, 40, 3, 2, 64, E8, BU)]
+    for c in cases:
+        c.require_one_launch()
     refs = []
     for c in cases:
         z = c.zbuf()
@@ -164,6 +173,7 @@ def test_one_launch_fallback_path(spin, monkeypatch):
     but a group's last arrival gives up waiting and quantises its whole group
     itself: the result is still bit-identical to the two-launch path."""
     c = _Case(445, 64, 16, 8, 1024, P2, B1)
+    c.require_one_launch()
     ref = c.zbuf()
     c.two_launch(c.wsbuf(), ref)
     monkeypatch.setenv("OPROJ_FUSED_DECODE_SPIN_LIMIT", spin)
@@ -183,6 +193,7 @@ def test_one_launch_graph_replays():
     """Captured in a HIP graph: every replay, with eager calls of the same
     entry point and new inputs between replays, equals the eager result."""
     c = _Case(450, 64, 16, 8, 1024, F32, B128)
+    c.require_one_launch()
     ws, z = c.wsbuf(), c.zbuf()
     c.one_launch(ws, z)
     torch.cuda.synchronize()
@@ -219,8 +230,11 @@ def test_eligibility_query_agrees_with_the_entry_point():
     """None for the decode batch; the compute-unit reason for a grid wider
     than the device, which the entry point refuses."""
     dec = ap.Shape(T=64, n_groups=16, heads_per_group=8, o_lora_rank=1024, max_pos=32768)
-    assert ap.oproj_fused_decode_unsupported(dec) is None
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus >= 16 * 16:
+        assert ap.oproj_fused_decode_unsupported(dec) is None
+    else:
+        assert "compute units" in ap.oproj_fused_decode_unsupported(dec)
     wide = ap.Shape(T=8, n_groups=cus // 16 + 1, heads_per_group=8, o_lora_rank=1024, max_pos=8192)
     assert "compute units" in ap.oproj_fused_decode_unsupported(wide)
 
