@@ -100,6 +100,11 @@ def test_grouped_gemm_validation(lib):
     assert _gemm(_shape(), ptrs=(0x1000, 0x1000, None, 0x1000, 0x1000)) == E_NULL
     assert _gemm(_shape(), ptrs=(0x1000, 0x1000, 0x1000, 0x1000, BAD)) == E_ALIGN
     assert _gemm(_shape(), ptrs=(0x1000, 0x1002, 0x1000, 0x1000, 0x1000)) == E_ALIGN
+    # 32-bit lane offsets: one group of D = 4096 holds at most 2^20 - 1 tokens,
+    # half as many with a token stride of two rows
+    big = dict(n_groups=1, heads_per_group=8, o_lora_rank=64)
+    assert _gemm(_shape(T=1 << 20, **big)) == E_SHAPE
+    assert _gemm(_shape(T=(1 << 19) + 1, **big), layout=_native.ActLayout(8192, 4096, 1, 1, 1 << 20)) == E_SHAPE
 
 
 def test_dense_gemm_validation(lib):

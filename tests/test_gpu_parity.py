@@ -252,6 +252,38 @@ def test_grouped_gemm_sampled_parity_full_size(name, n_samples):
     assert np.all(np.isfinite(zg))
 
 
+def test_grouped_gemm_at_the_offset_limit():
+    """The largest activation operand the GEMM accepts: one group with D = 4096
+    and T = 2^20 - 1 tokens, whose last row ends 4 KiB below 2^32 bytes (the
+    kernels address each operand as a uniform base plus 32-bit lane offsets;
+    one token more is refused).  Random FP8 codes and scales as inputs, outputs
+    sampled against the oracle on both sides of the 2^31-byte offset and at the
+    end of the operand."""
+    T, D, R = (1 << 20) - 1, 4096, 256
+    KB = D // 128
+    qa = wl.fp8_codes(wl.seed_of(90, 0), T * D).reshape(T, 1, D)
+    sa = (2.0 ** (-10.0 + 6.0 * wl.uniform(wl.seed_of(90, 1), T * KB))).astype(np.float32).reshape(T, 1, KB)
+    qw = wl.fp8_codes(wl.seed_of(90, 2), R * D).reshape(R, D)
+    sw = (2.0 ** (-12.0 + 4.0 * wl.uniform(wl.seed_of(90, 3), 2 * KB))).astype(np.float32).reshape(2, KB)
+    shp = ap.Shape(T=T, n_groups=1, heads_per_group=8, o_lora_rank=R, max_pos=1)
+    lay = ap.ActLayout(D, T * D, KB, T * KB, 1)  # token-major codes and scales
+    d_qa = _dev(qa)
+    z = torch.empty((T, 1, R), dtype=torch.int16, device=DEV)
+    ap.oproj_grouped_wo_a(shp, 0, d_qa, _dev(sa), lay, _dev(qw), _dev(sw), ap.OPROJ_WBLOCK_128x128, z)
+    torch.cuda.synchronize()
+    del d_qa
+    assert bool(torch.isfinite(z.view(torch.bfloat16)).all())
+    rng = np.random.default_rng(11)
+    idx = U.sample_triples(rng, T, 1, R, 3000)
+    edge = np.array([1, (1 << 19) - 1, 1 << 19, (1 << 19) + 1, T - 256, T - 2], np.int64)
+    idx[4:4 + edge.size, 0] = edge
+    zs = z[torch.from_numpy(idx[:, 0]).to(DEV), 0, torch.from_numpy(idx[:, 2]).to(DEV)]
+    got = U.bf16_bits_to_f64(_host(zs).view(np.uint16))
+    ref = oracle.grouped_gemm(qa, sa, qw, sw, 1, R, 128, idx=idx)
+    e = U.rel_max_err(got, ref)
+    assert e <= TOL, e
+
+
 def test_grouped_gemm_pow2_padded_input():
     """Pre-quantised [T, 10, D] input with NaN-poisoned padding groups, pow2
     scales and 1x128 weight blocks (block-scaled matrix-core path)."""

@@ -177,6 +177,16 @@ def uniform_int(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     return (lo + ((x * span) >> np.uint64(32))).astype(np.int64)
 
 
+def fp8_codes(seed: int, n: int) -> np.ndarray:
+    """n random e4m3fn codes (uint8): the bytes of the SplitMix64 stream, with
+    the two NaN patterns (S.1111.111) turned into +-448 (S.1111.110)."""
+    def chunk(s, m):  # chunk starts are multiples of 8 bytes
+        w = (m + 7) // 8
+        b = splitmix64(seed, s // 8, w).view(np.uint8)[:m]
+        return np.where((b & 0x7F) == 0x7F, b ^ np.uint8(1), b)
+    return _chunked(n, chunk, np.uint8)
+
+
 def cos_sin_table(max_pos: int, rope_dim: int, base: float = 10000.0) -> np.ndarray:
     """fp32 [max_pos, rope_dim]: cos of each pair's angle, then the sines."""
     half = rope_dim // 2
