@@ -153,6 +153,57 @@ def test_grouped_wo_a_bf16_prefill_sampled():
     assert e <= TOL, e
 
 
+def test_grouped_wo_a_bf16_at_the_offset_limit():
+    """The largest bf16 activation operand the grouped GEMM accepts: one group
+    with D = 4096 and T = 2^19 tokens, 4 GiB exactly (operands are addressed
+    as a base plus 32-bit lane offsets; one token more is refused).  Sampled
+    outputs against the oracle on both sides of the 2^31-byte offset and at
+    the end."""
+    T, D, R = 1 << 19, 4096, 128
+    w = wl.Workload(91, "limit", T=T, n_groups=1, heads_per_group=8, o_lora_rank=R, max_pos=1,
+                    positions="uniform")
+    x = wl.normal_bf16(wl.seed_of(91, 0), T * D)
+    wq = wl.wo_a_bf16(w)
+    d_x = _dev(x.view(np.int16))
+    z = torch.empty((T, 1, R), dtype=torch.int16, device=DEV)
+    ap.oproj_grouped_wo_a_bf16(_shape(w), d_x, None, _dev(wq.view(np.int16)), z)
+    torch.cuda.synchronize()
+    del d_x
+    assert bool(torch.isfinite(z.view(torch.bfloat16)).all())
+    idx = U.sample_triples(np.random.default_rng(12), T, 1, R, 2000)
+    edge = np.array([1, (1 << 18) - 1, 1 << 18, (1 << 18) + 1, T - 256, T - 2], np.int64)
+    idx[4:4 + edge.size, 0] = edge
+    zs = z[torch.from_numpy(idx[:, 0]).to(DEV), 0, torch.from_numpy(idx[:, 2]).to(DEV)]
+    got = U.bf16_bits_to_f64(_host(zs).view(np.uint16))
+    ref = oracle.grouped_gemm_bf16(x.reshape(T, 1, D), wq, 1, R, idx=idx)
+    e = U.rel_max_err(got, ref)
+    assert e <= TOL, e
+
+
+def test_dense_bf16_gemm_at_the_offset_limit():
+    """wo_b's kernel at its largest activation operand: M = 2^17 rows of
+    K = 16384 (4 GiB exactly), sampled against the oracle."""
+    M, N, K = 1 << 17, 64, 16384
+    x = wl.normal_bf16(wl.seed_of(92, 0), M * K)
+    wb = wl.bf16_matrix(wl.seed_of(92, 1), N, K, 0.02)
+    d_x = _dev(x.view(np.int16))
+    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    ap.oproj_dense_bf16_gemm(M, N, K, d_x, _dev(wb.view(np.int16)), y)
+    torch.cuda.synchronize()
+    del d_x
+    assert bool(torch.isfinite(y.view(torch.bfloat16)).all())
+    rng = np.random.default_rng(13)
+    m = rng.integers(0, M, 2000)
+    m[:6] = [0, (1 << 16) - 1, 1 << 16, (1 << 16) + 1, M - 2, M - 1]
+    j = rng.integers(0, N, 2000)
+    pairs = np.stack([m, j], axis=1).astype(np.int64)
+    ys = y[torch.from_numpy(m).to(DEV), torch.from_numpy(j).to(DEV)]
+    got = U.bf16_bits_to_f64(_host(ys).view(np.uint16))
+    ref = oracle.dense_gemm_bf16(x.reshape(M, K), wb, idx=pairs)
+    e = U.rel_max_err(got, ref)
+    assert e <= TOL, e
+
+
 def test_grouped_wo_a_bf16_group_isolation():
     w = wl.Workload(70, "iso", T=40, n_groups=3, heads_per_group=2, o_lora_rank=64, max_pos=4096,
                     positions="uniform")
