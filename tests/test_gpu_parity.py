@@ -145,6 +145,28 @@ def test_inv_rope_quant_ragged_shapes(T, G, hpg, pow2):
     U.assert_codes_parity(qg, qr)
 
 
+def test_inv_rope_quant_beyond_4gib_input():
+    """a1 + a2 on an input larger than 4 GiB (T = 4100 tokens of 1024 heads;
+    token t starts at t MiB), so that rows past 2^31 and 2^32 bytes are read
+    and group-major codes past 2^31 bytes are written.  Tokens on both sides
+    of those offsets and at the end against the oracle."""
+    w = wl.Workload(93, "big", T=4100, n_groups=128, heads_per_group=8, o_lora_rank=64, max_pos=32768,
+                    positions="uniform")
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_o = _dev(o.view(np.int16))
+    codes = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(_shape(w), 0, d_o, _dev(pos), _dev(tab), codes, scales)
+    torch.cuda.synchronize()
+    del d_o
+    sel = np.array([0, 1, 2047, 2048, 2049, 4095, 4096, 4097, 4098, 4099], np.int64)
+    tsel = torch.from_numpy(sel).to(DEV)
+    qg, sg = U.group_major_to_token_major(_host(codes[:, tsel, :]), _host(scales[:, :, tsel]))
+    qr, sr = oracle.inv_rope_quant(o[sel], pos[sel], tab, w.n_groups, w.heads_per_group)
+    U.assert_scales_bitexact(sg, sr)
+    U.assert_codes_parity(qg, qr)
+
+
 def test_inv_rope_quant_degenerate_blocks():
     """All-zero blocks, tiny and huge magnitudes, exact ties."""
     w = wl.Workload(60, "deg", T=6, n_groups=2, heads_per_group=2, o_lora_rank=64, max_pos=64,
