@@ -41,6 +41,30 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def device_info() -> dict:
+    """CU count and peak engine clock of device 0, read from the HIP runtime
+    the library links, and the dense matrix-core peaks they imply (gfx950:
+    8192 FP8 and 4096 BF16 FLOP per clock per CU).  The roofline fractions use
+    the published peaks above; these are printed beside them as a check."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+    except OSError:
+        return {}
+    v = ctypes.c_int(0)
+    info = {}
+    for key, attr in (("cus", 63), ("clock_khz", 5)):  # hipDeviceAttributeMultiprocessorCount, ...ClockRate
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) != 0:
+            return {}
+        info[key] = v.value
+    ghz = info["clock_khz"] / 1e6
+    info["fp8_peak_tflops"] = info["cus"] * ghz * 8192 / 1e3
+    info["bf16_peak_tflops"] = info["cus"] * ghz * 4096 / 1e3
+    log(f"device: {info['cus']} CUs at {ghz:.2f} GHz peak -> dense FP8 {info['fp8_peak_tflops']:.0f} TFLOP/s, "
+        f"BF16 {info['bf16_peak_tflops']:.0f} TFLOP/s")
+    return info
+
+
 def kernel_bytes_quant(w) -> int:
     """Algorithmic HBM bytes of a1+a2: read bf16 o, positions and the table
     rows; write FP8 codes and fp32 scales."""
@@ -234,6 +258,7 @@ def bench_bf16(args, w, torch, ap, wl, dev) -> int:
         "config": {"workload": f"{w.name} unquantised: T={T} n_groups={G} heads_per_group={w.heads_per_group} "
                                f"D={D} o_lora_rank={R}", "global_batch": T, "parallelism": "single GPU",
                    "copies_rotated": copies},
+        "device": device_info(),
         "roofline": {"bound": kd["bound"], "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": None},
         "cpu_baseline": None,
@@ -306,6 +331,7 @@ def bench_epilogue(args, w, torch, ap, wl, dev) -> int:
         "data": "synthetic (seeded SplitMix64 normals)",
         "config": {"workload": f"{w.name} epilogue producer: T={T} heads={H} n_groups={G} D={w.D}",
                    "global_batch": T, "parallelism": "single GPU", "copies_rotated": copies},
+        "device": device_info(),
         "roofline": {"bound": "hbm", "kernel": "inv_rope_quant_f32", "achieved": nb / (us * 1e3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": nb / (us * 1e3) / HBM_PEAK_GBS,
                      "traffic": None},
@@ -577,6 +603,7 @@ def main() -> int:
                    "global_batch": w.T, "parallelism": "single GPU",
                    "path": "one kernel (oproj_fused_decode)" if one_launch else "oproj_fused",
                    "step_TFLOP/s": gemm_tflops, "copies_rotated": copies},
+        "device": device_info(),
         "roofline": {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},
         "cpu_baseline": cpu,

@@ -57,3 +57,11 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_device_info_degrades_without_a_device():
+    """On a host without a GPU the device query returns an empty record
+    instead of raising; on a GPU it reports CUs, clock and implied peaks."""
+    import bench
+    info = bench.device_info()
+    assert info == {} or (info["cus"] > 0 and info["fp8_peak_tflops"] == 2 * info["bf16_peak_tflops"])
