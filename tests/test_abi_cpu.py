@@ -270,3 +270,36 @@ def test_torch_ops_checks_shapes_before_touching_a_device():
     o = torch.zeros((4, 6, 512), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         to.fused_inv_rope_fp8_quant(o, torch.zeros(4, dtype=torch.int64), torch.zeros((16, 64)), 2, 2)
+
+
+def test_product_and_oracle_share_no_code(lib):
+    """The HIP path never routes through the oracle and the two share no code:
+    no module of the package imports the oracle, no source of either side
+    includes a file of the other, and the built library neither exports nor
+    links any oracle symbol."""
+    import ast
+    import subprocess
+    pkg = os.path.join(ROOT, "attention_output_projection_amd")
+    orc = os.path.join(ROOT, "oracle")
+
+    def sources(d, exts):
+        for base, dirs, files in os.walk(d):
+            dirs[:] = [x for x in dirs if not x.startswith(("_build", "__pycache__"))]
+            for f in files:
+                if f.endswith(exts):
+                    yield os.path.join(base, f)
+
+    for path in sources(pkg, (".py",)):
+        for node in ast.walk(ast.parse(open(path).read())):
+            names = [a.name for a in node.names] if isinstance(node, ast.Import) else (
+                [node.module or ""] if isinstance(node, ast.ImportFrom) else [])
+            assert not any(n.split(".")[0] == "oracle" for n in names), path
+    for path in sources(pkg, (".hip", ".hpp", ".cpp", ".h")):
+        for inc in re.findall(r'#include\s+"([^"]+)"', open(path).read()):
+            assert "oracle" not in inc and "oproj_oracle" not in inc, (path, inc)
+    for path in sources(orc, (".py", ".c", ".h")):
+        text = open(path).read()
+        assert "attention_output_projection_amd" not in text and "csrc" not in text, path
+    assert not any(hasattr(lib, s) for s in ("orc_grouped_gemm", "orc_inv_rope_quant", "orc_irq_run"))
+    dyn = subprocess.run(["readelf", "-d", ap.library_path()], capture_output=True, text=True).stdout
+    assert "oracle" not in dyn
