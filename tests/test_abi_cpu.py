@@ -303,3 +303,15 @@ def test_product_and_oracle_share_no_code(lib):
     assert not any(hasattr(lib, s) for s in ("orc_grouped_gemm", "orc_inv_rope_quant", "orc_irq_run"))
     dyn = subprocess.run(["readelf", "-d", ap.library_path()], capture_output=True, text=True).stdout
     assert "oracle" not in dyn
+
+
+def test_missing_library_fails_loudly():
+    """Without the built HIP library every call raises: there is no fallback."""
+    import subprocess
+    import sys
+    code = ("import attention_output_projection_amd as ap, attention_output_projection_amd._native as n\n"
+            "n._LIB_PATH = '/nonexistent/liboproj.so'\n"
+            "ap.oproj_version()\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "RuntimeError" in r.stderr and "missing" in r.stderr
