@@ -148,3 +148,28 @@ def test_f32_producer_strided_layout_leaves_padding_alone():
     U.assert_scales_bitexact(sg[:, :G], sr)
     U.assert_codes_parity(qg[:, :G], qr)
     assert np.all(qg[:, G:] == 0x7F) and np.all(np.isnan(sg[:, G:]))
+
+
+def test_f32_producer_beyond_4gib_input():
+    """The producer on an fp32 input larger than 4 GiB (T = 2100 tokens of
+    1024 heads; token t starts at 2t MiB), so that rows past 2^31 and 2^32
+    bytes are read.  Tokens on both sides of those offsets and at the end
+    against the oracle."""
+    T, G, hpg = 2100, 128, 8
+    x = wl.normal_f32_bulk(wl.seed_of(760, 1), T * G * hpg * 512).reshape(T, G * hpg, 512)
+    tab = wl.cos_sin_table(32768, 64)
+    pos = wl.uniform_int(wl.seed_of(760, 2), T, 0, 32768).astype(np.int64)
+    shp = ap.Shape(T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=64, max_pos=tab.shape[0])
+    d_x = _dev(x)
+    codes = torch.empty((G, T, hpg * 512), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((G, hpg * 4, T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant_f32(shp, 0, d_x, _dev(pos), _dev(tab), codes, scales)
+    torch.cuda.synchronize()
+    del d_x
+    sel = np.array([0, 1, 1023, 1024, 1025, 2047, 2048, 2049, 2098, 2099], np.int64)
+    tsel = torch.from_numpy(sel).to(DEV)
+    qg = np.ascontiguousarray(codes[:, tsel, :].cpu().numpy().transpose(1, 0, 2))
+    sg = np.ascontiguousarray(scales[:, :, tsel].cpu().numpy().transpose(2, 0, 1))
+    qr, sr = oracle.inv_rope_quant_f32(x[sel], pos[sel], tab, G, hpg)
+    U.assert_codes_parity(qg, qr)
+    U.assert_scales_bitexact(sg, sr)
