@@ -105,6 +105,7 @@ CASES = [
     (5, 8, 4, 320, F32, B1),
     (64, 2, 2, 64, P2, BU),
     (63, 5, 2, 128, E8, B128),
+    (64, 256, 2, 64, F32, B128),  # the most groups the one-launch path takes, one workgroup per CU
 ]
 
 
