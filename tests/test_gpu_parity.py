@@ -360,6 +360,41 @@ def test_grouped_gemm_group_isolation_on_gpu():
     assert not np.array_equal(z1[:, 0], z2[:, 0])
 
 
+def test_fused_at_the_head_limit():
+    """The whole path at the most heads the library takes: 8192 groups of 8
+    heads (65536 heads, 2 GiB of FP8 weights), three tokens.  Codes and scales
+    in full, z sampled, against the oracle."""
+    T, G, hpg, R = 3, 8192, 8, 64
+    w = wl.Workload(94, "heads", T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=R, max_pos=4096,
+                    positions="uniform")
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    D, KB = w.D, w.KB
+    qw = wl.fp8_codes(wl.seed_of(94, 10), G * R * D).reshape(G * R, D)
+    sw = (2.0 ** (-12.0 + 4.0 * wl.uniform(wl.seed_of(94, 11), (G * R // 128) * KB))).astype(
+        np.float32).reshape(G * R // 128, KB)
+    shp = _shape(w)
+    nb = ap.oproj_fused_workspace_bytes(shp, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    z = torch.empty((T, G, R), dtype=torch.int16, device=DEV)
+    ap.oproj_fused(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), _dev(qw), _dev(sw),
+                   ap.OPROJ_WBLOCK_128x128, None, 0, ws, nb, z)
+    torch.cuda.synchronize()
+    ncode = T * G * D
+    codes = ws[:ncode].view(G, T, D)
+    soff = (ncode + 255) // 256 * 256
+    scales = ws[soff:soff + G * KB * T * 4].view(torch.float32).view(G, KB, T)
+    qg, sg = U.group_major_to_token_major(_host(codes), _host(scales))
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, hpg)
+    U.assert_scales_bitexact(sg, sr)
+    U.assert_codes_parity(qg, qr)
+    idx = U.sample_triples(np.random.default_rng(14), T, G, R, 4000)
+    idx[4:8, 1] = [0, 1, G - 2, G - 1]
+    zg = U.bf16_bits_to_f64(_host(z).view(np.uint16))
+    ref = oracle.grouped_gemm(qr, sr, qw, sw, G, R, 128, idx=idx)
+    e = U.rel_max_err(zg[idx[:, 0], idx[:, 1], idx[:, 2]], ref)
+    assert e <= TOL, e
+
+
 # ---------------------------------------------------------------- a4 and the fused entry point
 def test_dense_bf16_gemm_parity():
     rng = np.random.default_rng(9)
