@@ -308,3 +308,51 @@ def grouped_gemm_bf16(x_bf16, w_bf16, n_groups: int, o_lora_rank: int, idx=None,
         z[sel] = dense_gemm_bf16(np.ascontiguousarray(x[:, g, :]), w[g * R:(g + 1) * R], idx=pairs,
                                  nthreads=nthreads)
     return z
+
+
+# ---------------------------------------------------------------- whole-tensor forms (full-size parity)
+def dequant_act(qa, sa, n_groups: int | None = None) -> np.ndarray:
+    """decode(q) * scale for token-major activations [T, Gp, D] / [T, Gp, D/128]
+    (the scale multiplies its 128-wide block), fp64 [T, G, D]; only groups <
+    n_groups are decoded (a pre-quantised input's padding groups are dropped)."""
+    qa = np.asarray(qa, np.uint8)
+    sa = np.asarray(sa, np.float32)
+    G = qa.shape[1] if n_groups is None else n_groups
+    d = e4m3_decode(np.ascontiguousarray(qa[:, :G])).astype(np.float64)
+    return d * np.repeat(sa[:, :G].astype(np.float64), 128, axis=2)
+
+
+def grouped_gemm_full(qa, sa, qw, sw, n_groups: int, o_lora_rank: int,
+                      w_block_rows: int = 128) -> np.ndarray:
+    """The contraction of grouped_gemm over every output, for full-size
+    operands: each operand is dequantised once (decode(q) * scale, fp64) and
+    group g's output is one fp64 matrix product of its [T, D] activations with
+    weight rows g*R .. g*R+R-1 (vLLM API page
+    "vllm.models.deepseek_v4.nvidia.ops.o_proj", deep_gemm_fp8_o_proj: einsum
+    "bhr,hdr->bhd" over wo_a viewed [G, R, D]; the matrix product is numpy's).
+    Token-major [T, Gp, D] / [T, Gp, D/128] in (Gp >= n_groups), fp64 [T, G, R] out."""
+    G, R = n_groups, o_lora_rank
+    qw = np.asarray(qw, np.uint8)
+    assert qw.shape[0] == G * R and qa.shape[1] >= G
+    wd = dequant_weight(qw, sw, w_block_rows)
+    T = qa.shape[0]
+    z = np.empty((T, G, R), np.float64)
+    for g in range(G):
+        ad = dequant_act(qa[:, g:g + 1], sa[:, g:g + 1])[:, 0]
+        z[:, g, :] = ad @ wd[g * R:(g + 1) * R].T
+    return z
+
+
+def bf16_to_f64(h) -> np.ndarray:
+    """bf16 bit patterns -> fp64 values (exact: the bits are the top half of an fp32)."""
+    return (np.asarray(h, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def dense_gemm_bf16_full(x_bf16, w_bf16) -> np.ndarray:
+    """fp64 y = x @ w.T over every output for bf16 bits x[M, K], w[N, K] (the
+    linear layer wo_b of the sglang source page "python/sglang/srt/models/deepseek_v4.py",
+    MQALayer.forward, over the flattened z); the matrix product is numpy's."""
+    x = bf16_to_f64(x_bf16)
+    w = bf16_to_f64(w_bf16)
+    assert x.shape[1] == w.shape[1]
+    return x @ w.T

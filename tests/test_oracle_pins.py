@@ -489,6 +489,57 @@ def test_weight_quant_and_dequant_blocks():
     assert np.array_equal(d1, want1)
 
 
+def _pow2_ceil_frexp(x: np.ndarray) -> np.ndarray:
+    """Independent route to the power-of-two ceiling: frexp gives x = m * 2^e
+    with m in [0.5, 1); x is a power of two exactly when m == 0.5."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.where(m == 0.5, x, np.ldexp(1.0, e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_weight_quant_1x128_per_row_scales(pow2):
+    """1x128 mode: each row's block scale comes from THAT row's 128 values
+    (numpy's fp32 amax / 448, or its power-of-two ceiling), and each row's
+    block decodes to a max |code| of 448 (fp32) or within [224, 448] (pow2).
+    One large value planted in one row must change only that row's scale."""
+    rng = np.random.default_rng(21)
+    rows, K = 130, 384
+    wmat = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    wmat[5, 130] = 3.0  # row 5, block 1 only
+    q, s = oracle.quant_weight(wmat, 1, pow2=pow2)
+    assert s.shape == (rows, K // 128)
+    amax = np.abs(wmat.reshape(rows, K // 128, 128)).max(axis=2)
+    want = amax.astype(np.float32) / np.float32(448)
+    if pow2:
+        want = _pow2_ceil_frexp(want)
+    assert np.array_equal(s.view(np.uint32), want.view(np.uint32))
+    assert s[5, 1] > 20 * s[4, 1] and s[5, 1] > 20 * s[6, 1]
+    mx = np.abs(oracle.e4m3_decode(q).reshape(rows, K // 128, 128)).max(axis=2)
+    if pow2:
+        assert np.all((mx >= 224.0) & (mx <= 448.0))
+    else:
+        assert np.all(mx == 448.0)
+    # the codes are the e4m3fn roundings of w / scale, by brute-force search
+    quot = (wmat[3:6].reshape(3, K // 128, 128) / s[3:6, :, None]).astype(np.float32).ravel()
+    assert np.array_equal(q[3:6].ravel(), _nearest_even_by_search(quot))
+
+
+def test_weight_quant_1x128_golden_rows():
+    for line in _read_golden("weight_rows_1x128.txt"):
+        mode, ent, scl, codes = [p.strip() for p in line.split("|")]
+        row = np.zeros((1, 256), np.float32)
+        for kv in ent.split():
+            i, v = kv.split(":")
+            row[0, int(i)] = np.float32(float(v))
+        q, s = oracle.quant_weight(row, 1, pow2=(mode == "pow2"))
+        want_s = np.array([float(x) for x in scl.split()], np.float32)
+        assert np.array_equal(s[0], want_s), (line, s[0], want_s)
+        for kv in codes.split():
+            i, c = kv.split(":")
+            assert q[0, int(i)] == int(c, 16), (line, i, hex(q[0, int(i)]))
+        assert np.all(q[0, [j for j in range(256) if row[0, j] == 0]] == 0)
+
+
 # ---------------------------------------------------------------- a3: grouped contraction
 def _tiny_operands(T, G, D, R, seed, pad=0, brows=128, pow2=False):
     rng = np.random.default_rng(seed)
@@ -580,6 +631,48 @@ def test_grouped_gemm_sampled_equals_dense():
     idx = np.array([[0, 0, 0], [4, 1, 127], [2, 1, 5], [3, 0, 64]], np.int64)
     zs = oracle.grouped_gemm(qa, sa, qw, sw, G, R, idx=idx)
     assert np.array_equal(zs, z[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+@pytest.mark.parametrize("brows,pow2,pad", [(128, False, 0), (1, True, 2), (1, False, 1)])
+def test_grouped_gemm_full_equals_elementwise(brows, pow2, pad):
+    """The whole-tensor form (operands dequantised once, numpy fp64 product
+    per group) against the element-by-element C loop; NaN padding groups
+    must not reach it."""
+    T, G, D, R = 37, 3, 512, 160
+    qa, sa, qw, sw = _tiny_operands(T, G, D, R, 22, pad=pad, brows=brows, pow2=pow2)
+    qa[:, G:] = 0x7F
+    sa[:, G:] = np.nan
+    z = oracle.grouped_gemm(qa, sa, qw, sw, G, R, brows)
+    zf = oracle.grouped_gemm_full(qa, sa, qw, sw, G, R, brows)
+    assert zf.shape == (T, G, R) and np.all(np.isfinite(zf))
+    assert np.abs(zf - z).max() <= 1e-13 * np.abs(z).max()
+
+
+def test_grouped_gemm_full_exact_on_integer_operands():
+    """Codes of small integers and power-of-two scales make every partial sum
+    exact in fp64, so any order gives the same bits: the two forms must agree
+    exactly (a transposed operand or a wrong group slice cannot)."""
+    rng = np.random.default_rng(23)
+    T, G, D, R = 9, 2, 256, 128
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4], np.uint8)  # 0, +-1, +-2, 3, 4
+    qa = ints[rng.integers(0, ints.size, (T, G, D))]
+    qw = ints[rng.integers(0, ints.size, (G * R, D))]
+    sa = (2.0 ** rng.integers(-3, 3, (T, G, D // 128))).astype(np.float32)
+    sw = (2.0 ** rng.integers(-3, 3, (G * R // 128, D // 128))).astype(np.float32)
+    z = oracle.grouped_gemm(qa, sa, qw, sw, G, R, 128)
+    zf = oracle.grouped_gemm_full(qa, sa, qw, sw, G, R, 128)
+    assert np.array_equal(z, zf)
+    assert not np.array_equal(zf[:, 0], zf[:, 1])
+
+
+def test_dense_gemm_bf16_full_equals_elementwise():
+    rng = np.random.default_rng(24)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((33, 520)).astype(np.float32))
+    w = wl.f32_to_bf16_bits((rng.standard_normal((70, 520)) * 0.02).astype(np.float32))
+    y = oracle.dense_gemm_bf16(x, w)
+    yf = oracle.dense_gemm_bf16_full(x, w)
+    assert yf.shape == (33, 70)
+    assert np.abs(yf - y).max() <= 1e-13 * np.abs(y).max()
 
 
 # ---------------------------------------------------------------- a4: wo_b
