@@ -4,7 +4,33 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kernels.hpp"
+
+namespace oproj {
+
+DeviceInfo current_device_info() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];  // (cus << 8) | xcds, 0 until queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < kMaxDevices ? dev : kMaxDevices - 1;
+    int v = dev < kMaxDevices ? cached[slot].load(std::memory_order_relaxed) : 0;
+    if (v == 0) {
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1 ||
+            xcds > 255)
+            xcds = 1;
+        v = (cus << 8) | xcds;
+        if (dev < kMaxDevices) cached[slot].store(v, std::memory_order_relaxed);
+    }
+    return DeviceInfo{v >> 8, v & 0xFF};
+}
+
+}  // namespace oproj
 
 namespace {
 

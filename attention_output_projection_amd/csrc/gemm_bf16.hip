@@ -42,11 +42,13 @@ struct DParams {
     int64_t M, N, K;
     int64_t sx, sy, gx, gw, gy;  // row and group strides, elements
     int64_t G, mtiles, ntiles;   // tiles per group: mtiles x ntiles
+    int nxcd;                    // XCDs of the device (workgroups are dealt to them round-robin)
 };
 
-__device__ __forceinline__ int64_t xcd_remap_d(int64_t bid, int64_t nblocks) {
-    if (nblocks % 8 != 0) return bid;
-    return (bid % 8) * (nblocks / 8) + bid / 8;
+// Workgroup id -> tile id such that each XCD runs one contiguous range of tiles.
+__device__ __forceinline__ int64_t xcd_remap_d(int64_t bid, int64_t nblocks, int nxcd) {
+    if (nxcd <= 1 || nblocks % nxcd != 0) return bid;
+    return (bid % nxcd) * (nblocks / nxcd) + bid / nxcd;
 }
 
 template <int NI>
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int wm = wave & 3, wn = wave >> 2;
     const int64_t per = p.mtiles * p.ntiles;
-    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per);
+    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per, p.nxcd);
     const int64_t g = gid / per, id = gid - g * per;
     // band order: BAND M-tiles x all N-tiles, M fastest within the band
     const int64_t band = id / (BAND * p.ntiles);
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) 
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row group of the tile
     const bool copier = wave < 2;
     const int64_t per = p.mtiles * p.ntiles;
-    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per);
+    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per, p.nxcd);
     const int64_t g = gid / per, id = gid - g * per;
     const int64_t m0 = (id / p.ntiles) * XBM, n0 = (id % p.ntiles) * XBN;
     const int64_t kbytes = p.K * 2, xrow = p.sx * 2;
@@ -329,6 +331,8 @@ hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
     p.gw = a.gw;
     p.gy = a.gy;
     p.G = a.G;
+    const DeviceInfo dev = current_device_info();
+    p.nxcd = dev.xcds;
     if (a.M <= 128) {  // few tokens: 64x64 tiles, K split over two wave groups
         p.mtiles = (a.M + XBM - 1) / XBM;
         p.ntiles = (a.N + XBN - 1) / XBN;
@@ -338,12 +342,13 @@ hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
     }
     p.mtiles = (a.M + BM - 1) / BM;
     // 64-column tiles when 256-column tiles leave most of the chip idle;
-    // otherwise 224-column tiles when they fill the last round of 256
-    // workgroups better than 256-column tiles
+    // otherwise 224-column tiles when they fill the last round of workgroups
+    // (one per compute unit) better than 256-column tiles
     const int64_t t256 = a.G * p.mtiles * ((a.N + 255) / 256), t224 = a.G * p.mtiles * ((a.N + 223) / 224);
-    auto fill = [](int64_t tiles) { return (double)tiles / (double)(((tiles + 255) / 256) * 256); };
+    const int64_t cus = dev.cus;
+    auto fill = [cus](int64_t tiles) { return (double)tiles / (double)(((tiles + cus - 1) / cus) * cus); };
     int ni = 8;
-    if (t256 < 128)
+    if (t256 < cus / 2)
         ni = 2;
     else if (fill(t224) > fill(t256) + 0.02)
         ni = 7;

@@ -68,6 +68,7 @@ struct GParams {
     int kshift;   // activation scale words hold 1 << kshift K-blocks (0: fp32, 2: packed UE8M0)
     int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
     int spin = 0;  // one-launch path: polls of a group barrier before the fallback
+    int nxcd = 1;  // XCDs of the device (workgroups are dealt to them round-robin)
 };
 
 // Exponent byte (E8M0) of activation scale word `raw` for K-block kb: the
@@ -87,11 +88,11 @@ __device__ __forceinline__ v4f mfma_fp8_mx(const v8i& a, const v8i& b, const v4f
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
-// Spread consecutive workgroup ids over the 8 XCDs so that a contiguous range
-// of tiles (same group) runs on one XCD.
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks) {
-    if (nblocks % 8 != 0) return bid;
-    return (bid % 8) * (nblocks / 8) + bid / 8;
+// Workgroup ids are dealt to the XCDs round-robin: remap them so that each XCD
+// runs one contiguous range of tiles (the same group).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks, int nxcd) {
+    if (nxcd <= 1 || nblocks % nxcd != 0) return bid;
+    return (bid % nxcd) * (nblocks / nxcd) + bid / nxcd;
 }
 
 __device__ __forceinline__ int64_t wscale_index(const GParams& p, int64_t wrow, int64_t kb) {
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int wm = wave & 1, wn = wave >> 1;
     const int64_t nblocks = p.G * p.mtiles * p.ntiles;
-    const int64_t tile = xcd_remap(blockIdx.x, nblocks);
+    const int64_t tile = xcd_remap(blockIdx.x, nblocks, p.nxcd);
     const int64_t g = tile / (p.mtiles * p.ntiles);
     const int64_t mt = (tile / p.ntiles) % p.mtiles;
     const int64_t nt = tile % p.ntiles;
@@ -382,7 +383,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group within the tile
     const bool copier = wave < 2;
     const int64_t nblocks = p.G * p.mtiles * p.ntiles;
-    const int64_t tile = xcd_remap(blockIdx.x, nblocks);
+    const int64_t tile = xcd_remap(blockIdx.x, nblocks, p.nxcd);
     const int64_t g = tile / (p.mtiles * p.ntiles);
     const int64_t mt = (tile / p.ntiles) % p.mtiles;
     const int64_t nt = tile % p.ntiles;
@@ -689,6 +690,7 @@ hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a
     p.kbw = a.w_e8m0 ? KB / 4 : KB;
     p.mtiles = 1;
     p.ntiles = ntiles;
+    p.nxcd = current_device_info().xcds;
     // OPROJ_FUSED_DECODE_SPIN_LIMIT (diagnostics and tests) lowers the polls a
     // workgroup makes before it quantises its whole group itself; 0 sends every
     // workgroup but the last arrival of each group down that fallback
@@ -737,6 +739,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.kbw = a.w_e8m0 ? p.KB / 4 : p.KB;
     p.e8 = a.a_e8m0;
     p.kshift = a.a_e8m0 ? 2 : 0;
+    p.nxcd = current_device_info().xcds;
     // decode kernel for few tokens (the weight stream dominates), tile kernel otherwise
     const bool decode = a.T <= 128;
     if (decode) {

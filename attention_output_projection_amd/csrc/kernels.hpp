@@ -7,6 +7,15 @@
 
 namespace oproj {
 
+// Compute units and XCDs (chiplets with their own L2) of the current device,
+// queried from the HIP runtime once per device and cached; the launchers size
+// their grids and tile orders from it.
+struct DeviceInfo {
+    int cus;
+    int xcds;
+};
+DeviceInfo current_device_info();
+
 struct ActLayout {
     int64_t stride_t, stride_g;              // codes, bytes == elements
     int64_t s_stride_t, s_stride_g, s_stride_kb;  // scales, 4-byte words (fp32 or packed UE8M0)

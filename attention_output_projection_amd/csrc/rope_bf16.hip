@@ -135,7 +135,7 @@ hipError_t launch_inv_rope_bf16(const RopeBf16Args& a, hipStream_t stream) {
     p.nitems = (p.nrows + kRbRows - 1) / kRbRows;
     p.st = a.stride_t;
     p.sg = a.stride_g;
-    int64_t waves = 256 * OPROJ_RB_WAVES_PER_CU;
+    int64_t waves = (int64_t)current_device_info().cus * OPROJ_RB_WAVES_PER_CU;
     if (p.nitems < waves) waves = p.nitems;
     const dim3 grid((unsigned)((waves + kRbWaves - 1) / kRbWaves)), block(kRbWaves * 64);
     hipLaunchKernelGGL(inv_rope_bf16_kernel, grid, block, 0, stream, p);

@@ -135,16 +135,17 @@ __global__ __launch_bounds__(kWqThreads) void quantize_weight_kernel(const float
 #endif
 
 hipError_t launch_inv_rope_quant(const RopeQuantArgs& a, hipStream_t stream) {
+    const int cus = current_device_info().cus;
     int ch = rq::heads_per_item(a.hpg);  // 1, 2 or 4
     // small batches: two-head items when that still gives every item its own
     // wave within the occupancy limit (32 waves per CU) -- the kernel is then
     // latency-bound and more, smaller items finish sooner (measured)
-    const bool small = ch == 4 && a.T * a.G * (a.hpg / 2) <= 256 * 32;
+    const bool small = ch == 4 && a.T * a.G * (a.hpg / 2) <= (int64_t)cus * 32;
     if (small) ch = 2;
     const RQParams p = rq::make_params(a, ch);
-    // otherwise a fixed population of waves (OPROJ_Q_WAVES_PER_CU per CU on
-    // 256 CUs) walks the items
-    int64_t waves = 256 * OPROJ_Q_WAVES_PER_CU;
+    // otherwise a fixed population of waves (OPROJ_Q_WAVES_PER_CU per CU of
+    // the device) walks the items
+    int64_t waves = (int64_t)cus * OPROJ_Q_WAVES_PER_CU;
     if (small || p.nitems < waves) waves = p.nitems;
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kWaves * 64);

@@ -226,9 +226,11 @@ def dequant_weight(q, s, block_rows: int = 128) -> np.ndarray:
     """decode(q) * scale per block, fp64 (the scale is a multiplier)."""
     q = _c(q, np.uint8)
     rows, K = q.shape
-    d = e4m3_decode(q).astype(np.float64)
+    lut = e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float64)  # every code, decoded once
+    d = lut[q].reshape(rows, K // 128, 128)
     srow = np.repeat(np.asarray(s, np.float64), block_rows, axis=0)[:rows]
-    return d * np.repeat(srow, 128, axis=1)
+    d *= srow[:, :, None]
+    return d.reshape(rows, K)
 
 
 # ---------------------------------------------------------------- a3: grouped wo_a
@@ -317,9 +319,12 @@ def dequant_act(qa, sa, n_groups: int | None = None) -> np.ndarray:
     n_groups are decoded (a pre-quantised input's padding groups are dropped)."""
     qa = np.asarray(qa, np.uint8)
     sa = np.asarray(sa, np.float32)
-    G = qa.shape[1] if n_groups is None else n_groups
-    d = e4m3_decode(np.ascontiguousarray(qa[:, :G])).astype(np.float64)
-    return d * np.repeat(sa[:, :G].astype(np.float64), 128, axis=2)
+    T, Gp, D = qa.shape
+    G = Gp if n_groups is None else n_groups
+    lut = e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float64)  # every code, decoded once
+    d = lut[qa[:, :G]].reshape(T, G, D // 128, 128)
+    d *= sa[:, :G, :, None].astype(np.float64)
+    return d.reshape(T, G, D)
 
 
 def grouped_gemm_full(qa, sa, qw, sw, n_groups: int, o_lora_rank: int,

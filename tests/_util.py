@@ -84,3 +84,45 @@ def sample_triples(rng: np.random.Generator, T: int, G: int, R: int, n: int) -> 
     t[:4] = [0, T - 1, 0, T - 1]
     c[:4] = [0, R - 1, R - 1, 0]
     return np.stack([t, g, c], axis=1).astype(np.int64)
+
+
+def stratified_triples(rng: np.random.Generator, T: int, G: int, R: int, bm: int = 128, bn: int = 64,
+                       extra: int = 0) -> np.ndarray:
+    """(t, g, n) triples with one random element in every bm x bn block of
+    every group's [T, R] output (so every tile and every wave sub-tile of the
+    GEMM kernels is sampled), the last row and last column of each group, and
+    `extra` uniform draws."""
+    out = []
+    for g in range(G):
+        for m0 in range(0, T, bm):
+            for n0 in range(0, R, bn):
+                t = m0 + int(rng.integers(0, min(bm, T - m0)))
+                n = n0 + int(rng.integers(0, min(bn, R - n0)))
+                out.append((t, g, n))
+        out += [(T - 1, g, int(rng.integers(0, R))), (int(rng.integers(0, T)), g, R - 1),
+                (T - 1, g, R - 1), (0, g, 0)]
+    idx = np.array(out, np.int64)
+    if extra:
+        idx = np.concatenate([idx, sample_triples(rng, T, G, R, extra)])
+    return idx
+
+
+GUARD_BYTES = 4096
+GUARD_FILL = 0xA5
+
+
+def guarded_empty(shape, dtype, device):
+    """A tensor of `shape` followed by GUARD_BYTES guard bytes in one
+    allocation, every byte set to GUARD_FILL; returns (view, whole).  The
+    kernels get the view; guard_intact(whole, view) checks that nothing was
+    written past its end."""
+    import torch
+
+    nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    whole = torch.full((nbytes + GUARD_BYTES,), GUARD_FILL, dtype=torch.uint8, device=device)
+    return whole[:nbytes].view(dtype).view(*shape), whole
+
+
+def guard_intact(whole, view) -> bool:
+    nbytes = view.numel() * view.element_size()
+    return bool((whole[nbytes:] == GUARD_FILL).all().item())

@@ -52,9 +52,11 @@ def gpu_quant(w: wl.Workload, o: np.ndarray, pos: np.ndarray, tab: np.ndarray, p
     shp = _shape(w, o.shape[0])
     T = o.shape[0]
     d_o, d_pos, d_tab = _dev(o.view(np.int16)), _dev(pos), _dev(tab)
-    codes = torch.empty((w.n_groups, T, w.D), dtype=torch.uint8, device=DEV)
-    scales = torch.empty((w.n_groups, w.KB, T), dtype=torch.float32, device=DEV)
+    codes, gc = U.guarded_empty((w.n_groups, T, w.D), torch.uint8, DEV)
+    scales, gs = U.guarded_empty((w.n_groups, w.KB, T), torch.float32, DEV)
     ap.oproj_inv_rope_quant(shp, int(pow2), d_o, d_pos, d_tab, codes, scales)
+    torch.cuda.synchronize()
+    assert U.guard_intact(gc, codes) and U.guard_intact(gs, scales), "write past the end of an output"
     return U.group_major_to_token_major(_host(codes), _host(scales))
 
 
@@ -74,9 +76,11 @@ def gpu_gemm(w: wl.Workload, qa_tm: np.ndarray, sa_tm: np.ndarray, d_wq, d_ws, b
     T, Gp, D = qa_tm.shape
     KB = D // 128
     lay = ap.ActLayout(Gp * D, D, Gp * KB, KB, 1)
-    z = torch.empty((T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
+    z, gz = U.guarded_empty((T, w.n_groups, w.o_lora_rank), torch.int16, DEV)
     blk = ap.OPROJ_WBLOCK_1x128 if brows == 1 else ap.OPROJ_WBLOCK_128x128
     ap.oproj_grouped_wo_a(_shape(w, T), int(pow2), _dev(qa_tm), _dev(sa_tm), lay, d_wq, d_ws, blk, z)
+    torch.cuda.synchronize()
+    assert U.guard_intact(gz, z), "write past the end of z"
     return U.bf16_bits_to_f64(_host(z).view(np.uint16))
 
 
@@ -267,7 +271,7 @@ def test_grouped_gemm_sampled_parity_full_size(name, n_samples):
     z = torch.empty((w.T, w.n_groups, w.o_lora_rank), dtype=torch.int16, device=DEV)
     ap.oproj_grouped_wo_a(shp, 0, codes, scales, None, d_wq, d_ws, ap.OPROJ_WBLOCK_128x128, z)
     zg = U.bf16_bits_to_f64(_host(z).view(np.uint16))
-    idx = U.sample_triples(np.random.default_rng(7), w.T, w.n_groups, w.o_lora_rank, n_samples)
+    idx = U.stratified_triples(np.random.default_rng(7), w.T, w.n_groups, w.o_lora_rank, extra=n_samples)
     ref = oracle.grouped_gemm(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank, w.w_block_rows, idx=idx)
     e = U.rel_max_err(zg[idx[:, 0], idx[:, 1], idx[:, 2]], ref)
     assert e <= TOL, e
@@ -318,7 +322,7 @@ def test_grouped_gemm_pow2_padded_input():
     qpad[:, : w.n_groups], spad[:, : w.n_groups] = qr, sr
     d_wq, d_ws, qwr, swr = _weights_both(w)
     U.assert_scales_bitexact(_host(d_ws), swr)
-    idx = U.sample_triples(np.random.default_rng(8), w.T, w.n_groups, w.o_lora_rank, 3000)
+    idx = U.stratified_triples(np.random.default_rng(8), w.T, w.n_groups, w.o_lora_rank, extra=1000)
     ref = oracle.grouped_gemm(qpad, spad, qwr, swr, w.n_groups, w.o_lora_rank, 1, idx=idx)
     zg = gpu_gemm(w, qpad, spad, d_wq, d_ws, 1, True)
     assert np.all(np.isfinite(zg))
@@ -418,8 +422,10 @@ def test_dense_bf16_gemm_ragged(M, N, K):
     densely; the last two shapes take the 256x224 tiles."""
     x = wl.bf16_matrix(wl.seed_of(92, M), M, K, 1.0)
     wb = wl.bf16_matrix(wl.seed_of(93, N), N, K, 0.02)
-    y = torch.empty((M, N), dtype=torch.int16, device=DEV)
+    y, gy = U.guarded_empty((M, N), torch.int16, DEV)
     ap.oproj_dense_bf16_gemm(M, N, K, _dev(x.view(np.int16)), _dev(wb.view(np.int16)), y)
+    torch.cuda.synchronize()
+    assert U.guard_intact(gy, y), "write past the end of y"
     yg = U.bf16_bits_to_f64(_host(y).view(np.uint16))
     ref = oracle.dense_gemm_bf16(x, wb)
     e = U.rel_max_err(yg, ref)
@@ -704,3 +710,84 @@ def test_grouped_gemm_ue8m0_weights_equal_fp32_pow2(T, amode):
     ap.oproj_grouped_wo_a(shp, amode, codes, scales, None, wc, ws32, ap.OPROJ_WBLOCK_1x128, za)
     ap.oproj_grouped_wo_a(shp, amode, codes, scales, None, wc8, ws8, ap.OPROJ_WBLOCK_1x128_UE8M0, zb)
     assert torch.equal(za, zb)
+
+
+# ---------------------------------------------------------------- every output at full size
+# The whole-tensor oracle forms (each operand dequantised once, an fp64
+# product per group) make every output of the full-size workloads checkable.
+@pytest.mark.parametrize("name", ["prefill", "full"])
+def test_grouped_gemm_every_output_full_size(name):
+    """Every z of the prefill (T=8192) and full (T=4096) batches: end to end
+    (GPU codes, GPU weights) and isolated (oracle codes and weights into the
+    GPU GEMM), against the oracle chain."""
+    w = wl.WORKLOADS[name]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    U.assert_scales_bitexact(_host(d_ws), swr)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
+    ref = oracle.grouped_gemm_full(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank, w.w_block_rows)
+    shp = _shape(w)
+    codes = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=DEV)
+    ap.oproj_inv_rope_quant(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), codes, scales)
+    z, gz = U.guarded_empty((w.T, w.n_groups, w.o_lora_rank), torch.int16, DEV)
+    ap.oproj_grouped_wo_a(shp, 0, codes, scales, None, d_wq, d_ws, ap.OPROJ_WBLOCK_128x128, z)
+    torch.cuda.synchronize()
+    assert U.guard_intact(gz, z)
+    del codes, scales
+    e = U.rel_max_err(U.bf16_bits_to_f64(_host(z).view(np.uint16)), ref)
+    assert e <= TOL, f"end to end: E = {e:.3e}"
+    zi = gpu_gemm(w, qr, sr, _dev(qwr), _dev(swr), w.w_block_rows, w.pow2)
+    e = U.rel_max_err(zi, ref)
+    assert e <= TOL, f"isolated: E = {e:.3e}"
+
+
+def test_grouped_gemm_every_output_pow2_padded():
+    """Every z of the pow2 batch: the pre-quantised [T, 10, D] input (groups
+    8-9 NaN) with 1x128 power-of-two weight scales."""
+    w = wl.WORKLOADS["pow2"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    Gp = w.n_groups + w.pad_groups
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group, pow2=True)
+    qpad = np.full((w.T, Gp, w.D), 0x7F, np.uint8)
+    spad = np.full((w.T, Gp, w.KB), np.nan, np.float32)
+    qpad[:, : w.n_groups], spad[:, : w.n_groups] = qr, sr
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    U.assert_scales_bitexact(_host(d_ws), swr)
+    ref = oracle.grouped_gemm_full(qpad, spad, qwr, swr, w.n_groups, w.o_lora_rank, 1)
+    zg = gpu_gemm(w, qpad, spad, d_wq, d_ws, 1, True)
+    assert np.all(np.isfinite(zg))
+    e = U.rel_max_err(zg, ref)
+    assert e <= TOL, e
+
+
+def test_full_path_every_output_with_wo_b():
+    """The whole path at the full batch through oproj_fused with wo_b: every z
+    (read from the workspace, where a3 leaves it for a4) and every y, against
+    the oracle chain (oracle z rounded once to bf16, then fp64 wo_b)."""
+    w = wl.WORKLOADS["full"]
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    wob = wl.wo_b_bf16(w)
+    shp = _shape(w)
+    nbytes = ap.oproj_fused_workspace_bytes(shp, w.hidden)
+    ws, gws = U.guarded_empty((nbytes,), torch.uint8, DEV)
+    y, gy = U.guarded_empty((w.T, w.hidden), torch.int16, DEV)
+    ap.oproj_fused(shp, 0, _dev(o.view(np.int16)), _dev(pos), _dev(tab), d_wq, d_ws, 0,
+                   _dev(wob.view(np.int16)), w.hidden, ws, nbytes, y)
+    torch.cuda.synchronize()
+    assert U.guard_intact(gws, ws) and U.guard_intact(gy, y)
+    rnd = lambda v: (v + 255) // 256 * 256
+    zoff = rnd(w.T * w.n_groups * w.D) + rnd(w.T * w.n_groups * w.KB * 4)
+    zb_gpu = _host(ws[zoff: zoff + w.T * w.n_groups * w.o_lora_rank * 2]).view(np.uint16)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, w.n_groups, w.heads_per_group)
+    zr = oracle.grouped_gemm_full(qr, sr, qwr, swr, w.n_groups, w.o_lora_rank)
+    e = U.rel_max_err(U.bf16_bits_to_f64(zb_gpu).reshape(zr.shape), zr)
+    assert e <= TOL, f"z: E = {e:.3e}"
+    zb = oracle.f64_to_bf16(zr).reshape(w.T, w.n_groups * w.o_lora_rank)
+    del zr
+    yr = oracle.dense_gemm_bf16_full(zb, wob)
+    yg = U.bf16_bits_to_f64(_host(y).view(np.uint16))
+    assert np.all(np.isfinite(yg))
+    e = U.rel_max_err(yg, yr)
+    assert e <= TOL, f"y: E = {e:.3e}"
