@@ -69,6 +69,7 @@ struct GParams {
     int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
     int spin = 0;  // one-launch path: polls of a group barrier before the fallback
     int nxcd = 1;  // XCDs of the device (workgroups are dealt to them round-robin)
+    int pfd = 0;   // tile kernels: L2 prefetch distance in K-blocks (0: none)
 };
 
 // Exponent byte (E8M0) of activation scale word `raw` for K-block kb: the
@@ -120,15 +121,29 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 // pipeline is full, which at these tile sizes lasts longer than a K-block's
 // MFMAs; a copying wave therefore starts its MFMAs late, and its SIMD partner
 // (a wave that never copies) keeps the matrix core busy meanwhile.
+//
+// The CU's memory pipeline holds a fixed number of outstanding lines, so the
+// copy rate is set by their latency: lines that miss in L2 cost several times
+// a hit.  The tiles that run together on one XCD share slabs (the 4 N-tiles of
+// an M-tile its activation rows, 8 M-tiles a weight slab), so each tile also
+// touches its share of the shared slabs a few K-blocks ahead (one 4-byte load
+// per 128-byte line): one CU takes each miss, early, and the copies of every
+// CU then hit in L2.
+//
+// fp32 recipe: a subtile's fresh partials are folded into the accumulators
+// one subtile later (the last subtile of a K-block after the next barrier),
+// so the matrix core runs the next MFMAs while the promotion waits for them.
 constexpr int TBM = 256, TBN = 256, TNS = 2, TNW = 8;
 constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
 constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
 constexpr int TEROW = TBN + 8;      // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
+constexpr int kTilePrefetch = 2;    // L2 prefetch distance in K-blocks (measured best of 2, 3, 4, 6)
 static_assert(TBM * TEROW * 2 <= TNS * TSTAGE, "the epilogue tile fits in the ring");
 
 template <bool MX, bool W1>
 __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[TNS][TSTAGE];
+    __shared__ __attribute__((aligned(256))) uint8_t pf_sink[256];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
@@ -184,6 +199,30 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         dma4s(swbase + (kb >> p.wkshift) * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
     };
 
+    // L2 prefetch, shared out among the tiles that run together on one XCD
+    // (consecutive tile ids: the N-tiles of 8 M-tiles of one group): the
+    // N-tile nt < 4 of an M-tile touches activation rows 64*nt..64*nt+63 of
+    // the M-tile's slab, and M-tile mt touches weight rows 32*(mt%8) ..
+    // 32*(mt%8)+31 of the N-tile's slab, pfd K-blocks ahead of the copies,
+    // one 4-byte load per 128-byte line into a scratch LDS word.
+    const bool pfa = p.pfd > 0 && wave == 0 && nt < 4, pfw = p.pfd > 0 && wave == 1;
+    uint32_t pfoff = 0;
+    if (pfa) {
+        int64_t m = m0 + 64 * nt + lane;
+        m = m < p.T ? m : p.T - 1;
+        pfoff = (uint32_t)(m * p.st);
+    } else if (pfw) {
+        int64_t n = n0 + 32 * (mt & 7) + (lane & 31);
+        n = n < p.R ? n : p.R - 1;
+        pfoff = (uint32_t)(n * p.D);
+    }
+    const uint32_t sink = lds_offset(pf_sink);
+    auto prefetch = [&](int64_t kb) __attribute__((always_inline)) {
+        kb += p.pfd;
+        if (kb < p.KB) dma4s((pfa ? abase : wbase) + kb * 128, pfoff, sink);
+    };
+    const bool pf = pfa || pfw;  // wave-uniform
+
     if (copier) issue(0, 0);
 
     v4f acc[8][4];
@@ -205,10 +244,32 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
 
+    // fp32 recipe: the partials of the subtile issued last and their scale
+    // factors, folded into the accumulators one subtile later (the last
+    // subtile of a K-block across the barrier into the next K-block), so that
+    // the matrix core has the next subtile's MFMAs to run while they wait
+    v4f pend[4];
+    float psa[4] = {0.f, 0.f, 0.f, 0.f}, psw[4] = {0.f, 0.f, 0.f, 0.f};  // their row and column scales
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) pend[ni] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](int mi, int ni) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mi][ni][i] = __builtin_fmaf(pend[ni][i], psa[i] * psw[ni], acc[mi][ni][i]);
+    };
+
     for (int64_t kb = 0; kb < p.KB; ++kb) {
-        if (copier) wait_vmcnt<0>();   // this wave's copies of stage kb have landed
+        // this wave's copies of stage kb have landed (a prefetch issued after
+        // them may still be in flight: loads complete in order)
+        if (copier) {
+            if (pf && kb > 0 && kb + p.pfd < p.KB) wait_vmcnt<1>();
+            else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kb-1 are done
         __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
-        if (copier) issue(kb + 1, (int)((kb + 1) & 1));
+        if (copier) {
+            issue(kb + 1, (int)((kb + 1) & 1));
+            if (pf) prefetch(kb + 1);
+        }
         const uint8_t* st = ring[kb & 1];
         const uint8_t* sta = st + TSA + 128 * wm * 128;
         const uint8_t* stb = st + TSB + 64 * wn * 128;
@@ -257,16 +318,21 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
                     afn = frag(sta + (mi + 1) * 2048);
                     tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
                 }
-                v4f pp[4];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) pp[ni] = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int ni = 0; ni < 4; ++ni) {
+                    const v4f q = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+                    fold(mi == 0 ? 7 : mi - 1, ni);
+                    pend[ni] = q;
+                    if (mi == 0) psw[ni] = swv[ni];
+                }
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[mi][ni][i] = __builtin_fmaf(pp[ni][i], sa4[i] * swv[ni], acc[mi][ni][i]);
+                for (int i = 0; i < 4; ++i) psa[i] = sa4[i];
             }
         }
+    }
+    if constexpr (!MX) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) fold(7, ni);
     }
     wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
 
@@ -750,6 +816,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
         p.mtiles = (a.T + TBM - 1) / TBM;
         p.ntiles = (a.R + TBN - 1) / TBN;
         const dim3 grid((unsigned)(p.G * p.mtiles * p.ntiles));
+        p.pfd = kTilePrefetch;
         if (a.mx) {
             if (a.w_1x128)
                 hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, true>), grid, dim3(TNW * 64), 0, stream, p);

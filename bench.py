@@ -237,10 +237,18 @@ def timed_steps(torch, graphs, steps: int, warmup: int):
 
 def launch_average_us(torch, g, launches_per_replay: int, replays: int):
     """Average launch duration of a kernel: a graph of `launches_per_replay`
-    back-to-back launches replayed `replays` times between HIP events (after
-    one untimed replay); also the per-launch p10/p50/p90 over the replays."""
+    back-to-back launches replayed `replays` times back to back between two
+    HIP events (after one untimed replay).  Also the per-launch p10/p50/p90
+    over `replays` individually timed replays (each one pays its own ramp)."""
     g.replay()
     torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    mean = a.elapsed_time(b) * 1e3 / (replays * launches_per_replay)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
     for a, b in evs:
         a.record()
@@ -248,7 +256,7 @@ def launch_average_us(torch, g, launches_per_replay: int, replays: int):
         b.record()
     torch.cuda.synchronize()
     v = np.array([a.elapsed_time(b) * 1e3 / launches_per_replay for a, b in evs])
-    return float(v.mean()), pcts(v)
+    return float(mean), pcts(v)
 
 
 def roofline_of(kd: dict, bound: str, peak_mfma: float):
@@ -342,7 +350,6 @@ def run_fp8(args, w, torch, ap, wl, dev, steps: int, warmup: int, one_launch: bo
         g_gemm = G.capture([lambda c=c: gemm(c) for c in C])
         g_quant = None if w.prequantised else G.capture([lambda c=c: quant(c) for c in C])
         g_wob = G.capture([lambda c=c: wo_b(c) for c in C]) if wob is not None else None
-        g_one = G.capture([lambda c=c: step(c) for c in C]) if one_launch else None
 
         # replays must reproduce the eager result (eager work between replays)
         for _ in range(3):
@@ -364,6 +371,11 @@ def run_fp8(args, w, torch, ap, wl, dev, steps: int, warmup: int, one_launch: bo
         reps = max(args.kernel_reps, 1)
         kernels = {}
         pct = {"step": pcts(st_us)}
+        # the steps back to back (one graph of the whole rotation): what a
+        # stream of batches sustains when the host keeps ahead of the GPU
+        g_rot = G.capture([lambda c=c: step(c) for c in C])
+        rot_us, _ = launch_average_us(torch, g_rot, copies, reps)
+        log(f"steps back to back: {rot_us:.2f} us/step")
         gemm_bound = "hbm" if kernel_flops_gemm(w) / kernel_bytes_gemm(w) < \
             FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 else "mfma"
         t_gemm, pct["grouped_wo_a"] = launch_average_us(torch, g_gemm, copies, reps)
@@ -380,10 +392,10 @@ def run_fp8(args, w, torch, ap, wl, dev, steps: int, warmup: int, one_launch: bo
             fl = 2 * w.T * w.hidden * wrows
             kernels["wo_b"] = {"us": t_wob, "bound": "mfma", "flops": fl, "bytes": kernel_bytes_wo_b(w),
                                "TFLOP/s": fl / (t_wob * 1e6), "GB/s": kernel_bytes_wo_b(w) / (t_wob * 1e3)}
-        if g_one is not None:
+        if one_launch:
             # the one kernel of the step; its bytes are both steps' (the codes
             # and scales still go through the workspace)
-            t_one, pct["fused_decode"] = launch_average_us(torch, g_one, copies, reps)
+            t_one, pct["fused_decode"] = rot_us, pcts(st_us)
             nb = kernel_bytes_quant(w) + kernel_bytes_gemm(w)
             kernels["fused_decode"] = {"us": t_one, "bound": "hbm", "bytes": nb, "GB/s": nb / (t_one * 1e3)}
         log("kernel averages: " + ", ".join(f"{k} {v['us']:.2f} us" for k, v in kernels.items()))
@@ -425,7 +437,7 @@ def run_fp8(args, w, torch, ap, wl, dev, steps: int, warmup: int, one_launch: bo
                                + f" weight_blocks={'1x128' if w.w_block_rows == 1 else '128x128'}",
                    "global_batch": w.T, "parallelism": "single GPU", "path": step_desc,
                    "step_TFLOP/s": kernel_flops_gemm(w) / (med * 1e6), "copies_rotated": copies,
-                   "host_clock_us_per_step": host_us},
+                   "host_clock_us_per_step": host_us, "back_to_back_us_per_step": rot_us},
         "roofline": {"bound": kd["bound"], "kernel": dominant, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic},
         "cpu_baseline": cpu,
@@ -583,7 +595,9 @@ def bench_epilogue(args, w, torch, ap, wl, dev) -> int:
 def summary(r: dict) -> dict:
     """The figures of a secondary workload kept in the headline line."""
     return {"config": r["config"]["workload"], "value": r["value"], "unit": r["unit"],
-            "ms_per_step": r["ms_per_step"], "roofline": r["roofline"], "kernels": r["kernels"],
+            "ms_per_step": r["ms_per_step"],
+            "back_to_back_us_per_step": r["config"]["back_to_back_us_per_step"],
+            "roofline": r["roofline"], "kernels": r["kernels"],
             "p10_p50_p90_us": r["p10_p50_p90_us"]}
 
 
