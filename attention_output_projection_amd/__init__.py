@@ -10,6 +10,7 @@ library (``python -m attention_output_projection_amd.build``) and raises if it
 is missing.  There is no CPU fallback.
 """
 from ._native import (  # noqa: F401
+    OPROJ_NOALLOC_SCRATCH_BYTES,
     OPROJ_SCALE_E8M0,
     OPROJ_SCALE_FP32,
     OPROJ_SCALE_POW2,
@@ -28,6 +29,7 @@ from ._native import (  # noqa: F401
     oproj_fused_bf16,
     oproj_fused_decode,
     oproj_fused_decode_unsupported,
+    oproj_fused_noalloc,
     oproj_fused_bf16_workspace_bytes,
     oproj_fused_workspace_bytes,
     oproj_grouped_wo_a,

@@ -16,9 +16,10 @@ OPROJ_SCALE_E8M0 = 2
 OPROJ_WBLOCK_128x128 = 0
 OPROJ_WBLOCK_1x128 = 1
 OPROJ_WBLOCK_1x128_UE8M0 = 2
+OPROJ_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/oproj.h: the no-allocation entry point's scratch array
 
 _STATUS = {0: "OPROJ_OK", 1: "OPROJ_E_NULL", 2: "OPROJ_E_SHAPE", 3: "OPROJ_E_ALIGN",
-           4: "OPROJ_E_MODE", 5: "OPROJ_E_HIP"}
+           4: "OPROJ_E_MODE", 5: "OPROJ_E_HIP", 6: "OPROJ_E_SCRATCH"}
 
 
 class OprojError(RuntimeError):
@@ -126,6 +127,7 @@ def load_library():
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
             "oproj_inv_rope_quant_f32": (I32, [SP, I32, P, P, P, P, P, LP, P]),
             "oproj_fused_decode": (I32, [SP, I32, P, P, P, P, P, I32, P, SZ, P, P]),
+            "oproj_fused_noalloc": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, P]),
             "oproj_fused_decode_unsupported": (ctypes.c_char_p, [SP, I32, I32]),
             "oproj_quantize_weight": (I32, [I64, I64, I32, I32, P, P, P, P]),
             "oproj_status_string": (ctypes.c_char_p, [I32]),
@@ -231,6 +233,14 @@ def oproj_fused(shape: Shape, scale_mode: int, o, positions, cos_sin, w_codes, w
         _ptr(w_scales), w_block, _ptr(wo_b), hidden, _ptr(workspace), workspace_bytes, _ptr(out),
         _stream(stream))
     _check("oproj_fused", st)
+
+
+def oproj_fused_noalloc(shape: Shape, scale_mode: int, o, positions, cos_sin, w_codes, w_scales, w_block: int,
+                        wo_b, hidden: int, out, stream=None) -> None:
+    st = load_library().oproj_fused_noalloc(
+        ctypes.byref(shape._c()), scale_mode, _ptr(o), _ptr(positions), _ptr(cos_sin), _ptr(w_codes),
+        _ptr(w_scales), w_block, _ptr(wo_b), hidden, _ptr(out), _stream(stream))
+    _check("oproj_fused_noalloc", st)
 
 
 def oproj_fused_decode(shape: Shape, scale_mode: int, o, positions, cos_sin, w_codes, w_scales, w_block: int,

@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "liboproj.so")
 BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["rope_quant.hip", "rope_bf16.hip", "gemm_fp8.hip", "gemm_bf16.hip", "api.cpp"]
+SOURCES = ["rope_quant.hip", "rope_bf16.hip", "gemm_fp8.hip", "gemm_bf16.hip", "noalloc.hip", "api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     # matrix-core results stay in VGPRs (the block-scale promotion reads them)

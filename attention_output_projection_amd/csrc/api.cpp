@@ -117,6 +117,7 @@ const char* oproj_status_string(oproj_status s) {
         case OPROJ_E_ALIGN: return "misaligned pointer or stride";
         case OPROJ_E_MODE: return "unsupported mode or head geometry";
         case OPROJ_E_HIP: return "HIP launch error";
+        case OPROJ_E_SCRATCH: return "larger than the no-allocation scratch array";
     }
     return "unknown status";
 }

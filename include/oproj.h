@@ -53,7 +53,8 @@ typedef enum oproj_status {
     OPROJ_E_SHAPE = 2, /* sizes inconsistent or outside the supported range */
     OPROJ_E_ALIGN = 3, /* a pointer or stride breaks the 16-byte rule */
     OPROJ_E_MODE = 4,  /* unsupported scale mode / head geometry */
-    OPROJ_E_HIP = 5    /* a HIP launch or device query failed */
+    OPROJ_E_HIP = 5,   /* a HIP launch or device query failed */
+    OPROJ_E_SCRATCH = 6 /* the call needs more than the library's scratch array holds */
 } oproj_status;
 
 /* Scale recipe ([OPROJ] compute_fp8_einsum_recipe names two):
@@ -252,6 +253,27 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
                          const int64_t* positions, const float* cos_sin, const void* w_codes,
                          const void* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
                          void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* Size of the device array oproj_fused_noalloc uses as its workspace, one per
+ * GPU, held until the process ends. */
+#define OPROJ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* oproj_fused without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, kernels and result as oproj_fused
+ * (out: z bf16 [T][G][R], or y bf16 [T][hidden] when wo_b != NULL); the
+ * workspace is a device array the library holds per GPU, of
+ * OPROJ_NOALLOC_SCRATCH_BYTES.  Allocates nothing: no hipMalloc, no hipFree.
+ * A call whose oproj_fused_workspace_bytes(shape, wo_b ? hidden : 0) exceeds
+ * that size returns OPROJ_E_SCRATCH and enqueues nothing.  Every call on one
+ * GPU shares that GPU's array (whose contents persist between calls): calls
+ * that overlap in time on one GPU, on any streams, race and give wrong
+ * results.  The first call on each GPU looks up its array's device address
+ * (hipGetSymbolAddress; OPROJ_E_HIP if that fails). */
+oproj_status oproj_fused_noalloc(const oproj_shape* shape, int32_t scale_mode, const void* o,
+                                 const int64_t* positions, const float* cos_sin, const void* w_codes,
+                                 const void* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
+                                 void* out, void* stream);
 
 /* Steps a1 + a2 + a3 of oproj_fused (wo_b == NULL) in ONE kernel launch, for
  * decode-sized batches, where the launch and the quantisation round trip sit

@@ -193,6 +193,25 @@ def test_fused_workspace_and_validation(lib):
     assert fused(_shape(T=0), 0) == E_OK
 
 
+def test_fused_noalloc_validation(lib):
+    """The no-allocation entry point refuses a call larger than its scratch
+    array, and T == 0 / invalid shapes as oproj_fused does, all before any
+    device work (so on a host without a GPU)."""
+    P = 0x1000
+
+    def noalloc(shape, wo_b=None, hidden=0, mode=0):
+        return _raw("oproj_fused_noalloc", ctypes.byref(shape._c()), mode, P, P, P, P, P, 0, wo_b, hidden, P,
+                    None)
+
+    big = _shape(T=1024, n_groups=16, heads_per_group=8, o_lora_rank=1024, max_pos=32768)
+    assert ap.oproj_fused_workspace_bytes(big, 0) > ap.OPROJ_NOALLOC_SCRATCH_BYTES
+    assert noalloc(big) == 6
+    assert "scratch" in ap.oproj_status_string(6)
+    assert noalloc(_shape(o_lora_rank=10)) == E_SHAPE
+    assert noalloc(_shape(T=0)) == E_OK
+    assert noalloc(_shape(), mode=9) == E_MODE
+
+
 def test_fused_decode_validation(lib):
     """The one-launch entry point's checks, all made before anything touches
     the device: shape limits, head geometry, pointers, workspace size."""
