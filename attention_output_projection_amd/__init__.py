@@ -28,6 +28,7 @@ from ._native import (  # noqa: F401
     oproj_fused,
     oproj_fused_bf16,
     oproj_fused_decode,
+    oproj_fused_decode_workspace_bytes,
     oproj_fused_decode_unsupported,
     oproj_fused_noalloc,
     oproj_fused_bf16_workspace_bytes,

@@ -122,6 +122,7 @@ def load_library():
             "oproj_grouped_wo_a_bf16": (I32, [SP, P, BP, P, P, P]),
             "oproj_dense_bf16_gemm": (I32, [I64, I64, I64, P, P, P, P]),
             "oproj_fused_workspace_bytes": (SZ, [SP, I64]),
+            "oproj_fused_decode_workspace_bytes": (SZ, [SP]),
             "oproj_fused_bf16_workspace_bytes": (SZ, [SP, I64]),
             "oproj_fused_bf16": (I32, [SP, P, P, P, P, P, I64, P, SZ, P, P]),
             "oproj_fused": (I32, [SP, I32, P, P, P, P, P, I32, P, I64, P, SZ, P, P]),
@@ -255,6 +256,10 @@ def oproj_fused_decode_unsupported(shape: Shape, scale_mode: int = 0, w_block: i
     """None when oproj_fused_decode can take this shape on the current device, else the reason."""
     r = load_library().oproj_fused_decode_unsupported(ctypes.byref(shape._c()), scale_mode, w_block)
     return None if r is None else r.decode()
+
+
+def oproj_fused_decode_workspace_bytes(shape: Shape) -> int:
+    return load_library().oproj_fused_decode_workspace_bytes(ctypes.byref(shape._c()))
 
 
 def oproj_fused_bf16_workspace_bytes(shape: Shape, hidden: int = 0) -> int:

@@ -420,6 +420,12 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
                                  out, stream);
 }
 
+size_t oproj_fused_decode_workspace_bytes(const oproj_shape* shape) {
+    const size_t b = oproj_fused_workspace_bytes(shape, 0);
+    if (b == 0) return 0;
+    return b + round_up((size_t)shape->n_groups * oproj::kFusedDecodeSyncBytesPerGroup);
+}
+
 oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, const void* o,
                                 const int64_t* positions, const float* cos_sin, const void* w_codes,
                                 const void* w_scales, int32_t w_block, void* workspace,
@@ -431,14 +437,18 @@ oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, co
     if (shape->T > 64 || shape->n_groups > 256) return OPROJ_E_SHAPE;
     if (shape->heads_per_group != 2 && shape->heads_per_group % 4 != 0) return OPROJ_E_MODE;
     if (shape->T == 0) return OPROJ_OK;
+    if (workspace && workspace_bytes < oproj_fused_decode_workspace_bytes(shape)) return OPROJ_E_SHAPE;
     oproj::RopeQuantArgs qa;
     oproj::GroupedGemmArgs ga;
     void* zbuf = nullptr;
     if ((st = prep_fused(shape, scale_mode, o, positions, cos_sin, w_codes, w_scales, w_block, 0, workspace,
                          workspace_bytes, z, &qa, &ga, &zbuf)) != OPROJ_OK)
         return st;
+    // the groups' barrier words follow the codes and scales
+    uint64_t* sync = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
+                                                 oproj_fused_workspace_bytes(shape, 0));
     bool launched = false;
-    if ((st = from_hip(oproj::launch_fused_decode(qa, ga, static_cast<hipStream_t>(stream), &launched))) !=
+    if ((st = from_hip(oproj::launch_fused_decode(qa, ga, sync, static_cast<hipStream_t>(stream), &launched))) !=
         OPROJ_OK)
         return st;
     return launched ? OPROJ_OK : OPROJ_E_SHAPE;

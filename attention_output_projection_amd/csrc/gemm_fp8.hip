@@ -68,6 +68,7 @@ struct GParams {
     int kshift;   // activation scale words hold 1 << kshift K-blocks (0: fp32, 2: packed UE8M0)
     int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
     int spin = 0;  // one-launch path: polls of a group barrier before the fallback
+    uint64_t* sync = nullptr;  // one-launch path: the groups' barrier words (caller's workspace)
     int nxcd = 1;  // XCDs of the device (workgroups are dealt to them round-robin)
     int pfd = 0;   // tile kernels: L2 prefetch distance in K-blocks (0: none)
 };
@@ -393,17 +394,17 @@ constexpr int DPROW = DBN + 4;  // fp32 per row of an epilogue partial tile (pad
 static_assert(DKS * DBM * DPROW * 4 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
 
 // Barrier state of the one-launch decode path: one 64-bit word per group, on
-// a cache line of its own (zero when the library loads).  Fields, low bit
-// first: arrivals at the current barrier (9 bits), the sum of the arrivals'
-// XCD numbers (12 bits) and of their squares (16 bits), whether the previous
-// barrier's arrivals ran on more than one XCD (1 bit), and the count of
-// barriers the group has completed (its epoch, the top 26 bits).  One
-// returning atomic add per arrival; the last arrival replaces the word with
-// the next epoch and its XCD flag in a second add, so every launch leaves
-// the word ready for the next one whatever its group size.
+// a cache line of its own, in the caller's workspace (zero before the first
+// call with that workspace).  Fields, low bit first: arrivals at the current
+// barrier (9 bits), the sum of the arrivals' XCD numbers (12 bits) and of
+// their squares (16 bits), whether the previous barrier's arrivals ran on
+// more than one XCD (1 bit), and the count of barriers the group has completed
+// (its epoch, the top 26 bits).  One returning atomic add per arrival; the
+// last arrival replaces the word with the next epoch and its XCD flag in a
+// second add, so every launch leaves the word ready for the next one whatever
+// its group size.  Launches with distinct workspaces never meet.
 constexpr int kMaxFusedGroups = 256;
 constexpr int kSyncStride = 16;  // 128-byte cache line
-__device__ uint64_t g_group_sync[kSyncStride * kMaxFusedGroups];
 constexpr int kGroupSpinLimit = 4096;  // bounded wait: a missing workgroup is covered by a fallback
 constexpr int kSyncSum = 9, kSyncSq = 21, kSyncMixed = 37, kSyncEpoch = 38;
 
@@ -414,8 +415,8 @@ __device__ __forceinline__ uint64_t xcc_id() { return __builtin_amdgcn_s_getreg(
 // others.  Returns 0 when every workgroup of the group arrived and all ran on
 // one XCD, 1 when they arrived from several XCDs, 2 when the wait gave up
 // (the caller then does the missing work itself).  Called by one thread.
-__device__ int group_barrier(int64_t g, int64_t n, int spin) {
-    uint64_t* word = &g_group_sync[kSyncStride * g];
+__device__ int group_barrier(uint64_t* sync, int64_t g, int64_t n, int spin) {
+    uint64_t* word = sync + kSyncStride * g;
     const uint64_t x = xcc_id();
     const uint64_t inc = 1ull + (x << kSyncSum) + ((x * x) << kSyncSq);
     const uint64_t old = __hip_atomic_fetch_add(word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -559,7 +560,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         quantise(nt * 8 + (tid >> 6), p.ntiles * 8);
         __shared__ int sync_state;
         __syncthreads();
-        if (tid == 0) sync_state = group_barrier(g, p.ntiles, p.spin);
+        if (tid == 0) sync_state = group_barrier(p.sync, g, p.ntiles, p.spin);
         __syncthreads();
         if (sync_state == 2) {
             // a workgroup of the group did not arrive in time: quantise the
@@ -725,8 +726,8 @@ const char* fused_decode_unfit(int64_t T, int64_t G, int64_t hpg, int64_t R) {
     return nullptr;
 }
 
-hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a, hipStream_t stream,
-                               bool* launched) {
+hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a, uint64_t* sync,
+                               hipStream_t stream, bool* launched) {
     *launched = false;
     if (fused_decode_unfit(a.T, a.G, qa.hpg, a.R)) return hipSuccess;
     const int64_t KB = a.D / 128;
@@ -757,6 +758,7 @@ hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a
     p.mtiles = 1;
     p.ntiles = ntiles;
     p.nxcd = current_device_info().xcds;
+    p.sync = sync;
     // OPROJ_FUSED_DECODE_SPIN_LIMIT (diagnostics and tests) lowers the polls a
     // workgroup makes before it quantises its whole group itself; 0 sends every
     // workgroup but the last arrival of each group down that fallback

@@ -63,10 +63,12 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t s);
 // One launch for both steps at few tokens (quantisation into the default
 // layout of q's buffers, then the grouped GEMM reading them).  *launched is
 // false, and nothing is enqueued, when the shape does not fit that path.
-// Launches of this path on one GPU must not overlap in time (they share the
-// per-group barrier words the library holds on each device).
-hipError_t launch_fused_decode(const RopeQuantArgs& q, const GroupedGemmArgs& a, hipStream_t s,
+// `sync` holds one 128-byte barrier word line per group (zero before the first
+// launch with it; each launch leaves it ready for the next); launches that
+// overlap in time need distinct `sync` regions.
+hipError_t launch_fused_decode(const RopeQuantArgs& q, const GroupedGemmArgs& a, uint64_t* sync, hipStream_t s,
                                bool* launched);
+constexpr size_t kFusedDecodeSyncBytesPerGroup = 128;
 // Why that path cannot take a call of this shape on the current device
 // (static text), or nullptr when it can.
 const char* fused_decode_unfit(int64_t T, int64_t G, int64_t hpg, int64_t R);

@@ -173,18 +173,22 @@ def deep_gemm_fp8_o_proj(o: torch.Tensor, positions: torch.Tensor, cos_sin_cache
               wo_b=wo_b)
     hidden = 0 if wo_b is None else wo_b.shape[0]
     ws_bytes = n.oproj_fused_workspace_bytes(shape, hidden)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
     o = o.contiguous()
     if wo_b is None:
         z = torch.empty((T, n_groups, o_lora_rank), dtype=torch.bfloat16, device=o.device)
         if one_launch and n.oproj_fused_decode_unsupported(shape, scale_mode, w_block) is None:
+            # a fresh workspace: its barrier words start at zero
+            dbytes = n.oproj_fused_decode_workspace_bytes(shape)
+            ws = torch.zeros(dbytes, dtype=torch.uint8, device=o.device)
             n.oproj_fused_decode(shape, scale_mode, o, positions, cos_sin_cache, w_codes, w_scales, w_block,
-                                 ws, ws_bytes, z)
+                                 ws, dbytes, z)
         else:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
             n.oproj_fused(shape, scale_mode, o, positions, cos_sin_cache, w_codes, w_scales, w_block, None, 0,
                           ws, ws_bytes, z)
         return z
     y = torch.empty((T, hidden), dtype=torch.bfloat16, device=o.device)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=o.device)
     n.oproj_fused(shape, scale_mode, o, positions, cos_sin_cache, w_codes, w_scales, w_block, wo_b.contiguous(),
                   hidden, ws, ws_bytes, y)
     return y

@@ -291,6 +291,8 @@ def run_fp8(args, w, torch, ap, wl, dev, steps: int, warmup: int, one_launch: bo
     srows = wrows if w.w_block_rows == 1 else (wrows + 127) // 128
     hidden = w.hidden if wob is not None else 0
     ws_bytes = ap.oproj_fused_workspace_bytes(shp, hidden)
+    if one_launch:  # the codes and scales, then the groups' barrier words (zeroed once below)
+        ws_bytes = ap.oproj_fused_decode_workspace_bytes(shp)
     # the padded token-major layout of a pre-quantised input: [T, Gp, D] codes, [T, Gp, KB] scales
     pad_lay = ap.ActLayout(Gp * w.D, w.D, Gp * w.KB, w.KB, 1) if w.prequantised else None
     C = []
@@ -311,7 +313,7 @@ def run_fp8(args, w, torch, ap, wl, dev, steps: int, warmup: int, one_launch: bo
             c["o"] = t(o.view(np.int16))
             c["codes"] = torch.empty((w.n_groups, w.T, w.D), dtype=torch.uint8, device=dev)
             c["scales"] = torch.empty((w.n_groups, w.KB, w.T), dtype=torch.float32, device=dev)
-            c["work"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            c["work"] = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         if wob is not None:
             c["wob"] = t(wob.view(np.int16))
             c["y"] = torch.empty((w.T, w.hidden), dtype=torch.int16, device=dev)

@@ -281,19 +281,24 @@ oproj_status oproj_fused_noalloc(const oproj_shape* shape, int32_t scale_mode, c
  * the grouped GEMM directly).  Each workgroup first quantises its share of
  * its group's activations into the workspace, meets the group's other
  * workgroups at a barrier, then runs its output tile of the grouped GEMM.
- * Arguments, workspace (oproj_fused_workspace_bytes(shape, 0)) and result are
- * those of oproj_fused with wo_b == NULL; z is bit-identical to it.
+ * Arguments and result are those of oproj_fused with wo_b == NULL; z is
+ * bit-identical to it.  The workspace (oproj_fused_decode_workspace_bytes)
+ * holds the codes and scales of oproj_fused followed by the groups' barrier
+ * words: that last region (n_groups * 128 bytes, 256-byte rounded) must be
+ * zero before the first call with a workspace, and each call leaves it ready
+ * for the next one.
  * Supported: T <= 64, n_groups <= 256, heads_per_group 2 or a multiple of 4,
  * D / 128 >= 8, and n_groups * ceil(o_lora_rank / 64) workgroups no more than
  * the device's compute units (every workgroup resident at once); otherwise
  * OPROJ_E_SHAPE (or OPROJ_E_MODE for the head geometry) and nothing is
  * enqueued.
- * Concurrency: calls on one device must not overlap in time, on any streams:
- * they share the library's per-group barrier words on that device.  A
+ * Concurrency: calls with distinct workspaces are independent and may
+ * overlap; calls that share a workspace must not overlap in time.  A
  * workgroup that waits too long at its barrier quantises its whole group
  * itself, so a slow neighbour costs time, never correctness.  The environment
  * variable OPROJ_FUSED_DECODE_SPIN_LIMIT (read at each call; diagnostics and
  * tests) lowers the number of polls before that fallback, down to 0. */
+size_t oproj_fused_decode_workspace_bytes(const oproj_shape* shape);
 oproj_status oproj_fused_decode(const oproj_shape* shape, int32_t scale_mode, const void* o,
                                 const int64_t* positions, const float* cos_sin, const void* w_codes,
                                 const void* w_scales, int32_t w_block, void* workspace,

@@ -219,10 +219,15 @@ def test_fused_decode_validation(lib):
     n0 = ap.oproj_fused_workspace_bytes(shp, 0)
     P = 0x1000
 
-    def dec(shape, ws_bytes=n0, mode=0, wblock=0, ws=P, o=P, z=P):
+    def dec(shape, ws_bytes=None, mode=0, wblock=0, ws=P, o=P, z=P):
+        if ws_bytes is None:
+            ws_bytes = ap.oproj_fused_decode_workspace_bytes(shape)
         return _raw("oproj_fused_decode", ctypes.byref(shape._c()), mode, o, P, P, P, P, wblock, ws, ws_bytes,
                     z, None)
 
+    nd = ap.oproj_fused_decode_workspace_bytes(shp)
+    assert nd == n0 + 16 * 128  # the groups' barrier words after the codes and scales
+    assert dec(shp, ws_bytes=nd - 1) == E_SHAPE
     assert dec(_shape(T=0), 0, o=None, z=None, ws=None) == E_OK
     assert dec(_shape(T=65, n_groups=1, heads_per_group=8, o_lora_rank=64)) == E_SHAPE
     assert dec(_shape(T=8, n_groups=257, heads_per_group=8, o_lora_rank=64)) == E_SHAPE

@@ -2,8 +2,8 @@
 grouped GEMM in one kernel) against the two-launch oproj_fused, bit for bit,
 and against the oracle chain: every scale recipe and weight-block mode,
 ragged token counts, each supported head geometry, bad positions, calls
-back to back with changing group sizes, graph replays and the shapes it
-refuses."""
+back to back with changing group sizes, calls overlapping on two streams with
+their own workspaces, graph replays and the shapes it refuses."""
 from __future__ import annotations
 
 import numpy as np
@@ -58,6 +58,7 @@ class _Case:
         ap.oproj_quantize_weight(rows, K, wblock, mode, _dev(self.wmat), self.d_wq, self.d_ws)
         self.shp = ap.Shape(T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=R, max_pos=max_pos)
         self.nbytes = ap.oproj_fused_workspace_bytes(self.shp, 0)
+        self.dbytes = ap.oproj_fused_decode_workspace_bytes(self.shp)
         self.d_o, self.d_pos, self.d_tab = _dev(self.o.view(np.int16)), _dev(self.pos), _dev(self.tab)
 
     def zbuf(self):
@@ -66,6 +67,13 @@ class _Case:
     def wsbuf(self):
         return torch.full((self.nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
 
+    def dwsbuf(self):
+        """A one-launch workspace: garbage where the codes and scales go, the
+        barrier words zeroed (as a caller does once per workspace)."""
+        ws = torch.full((self.dbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        ws[self.nbytes:].zero_()
+        return ws
+
     def require_one_launch(self):
         why = ap.oproj_fused_decode_unsupported(self.shp, self.mode, self.wblock)
         if why is not None:  # e.g. a partitioned device with fewer compute units
@@ -73,7 +81,7 @@ class _Case:
 
     def one_launch(self, ws, z):
         ap.oproj_fused_decode(self.shp, self.mode, self.d_o, self.d_pos, self.d_tab, self.d_wq, self.d_ws,
-                              self.wblock, ws, self.nbytes, z)
+                              self.wblock, ws, self.dbytes, z)
 
     def two_launch(self, ws, z):
         ap.oproj_fused(self.shp, self.mode, self.d_o, self.d_pos, self.d_tab, self.d_wq, self.d_ws,
@@ -113,7 +121,7 @@ CASES = [
 def test_one_launch_equals_two_launches_and_oracle(T, G, hpg, R, mode, wblock):
     c = _Case(400 + T + 7 * G + hpg, T, G, hpg, R, mode, wblock)
     c.require_one_launch()
-    ws1, z1 = c.wsbuf(), c.zbuf()
+    ws1, z1 = c.dwsbuf(), c.zbuf()
     c.one_launch(ws1, z1)
     ws2, z2 = c.wsbuf(), c.zbuf()
     c.two_launch(ws2, z2)
@@ -134,7 +142,7 @@ def test_one_launch_bad_positions():
     c = _Case(431, 24, 4, 8, 256, F32, B128, bad_positions=True)
     c.require_one_launch()
     z1, z2 = c.zbuf(), c.zbuf()
-    c.one_launch(c.wsbuf(), z1)
+    c.one_launch(c.dwsbuf(), z1)
     c.two_launch(c.wsbuf(), z2)
     torch.cuda.synchronize()
     assert torch.equal(z1, z2)
@@ -156,7 +164,7 @@ def test_one_launch_back_to_back_changing_group_sizes():
         c.two_launch(c.wsbuf(), z)
         refs.append(z)
     outs = [[c.zbuf() for _ in range(14)] for c in cases]
-    wss = [c.wsbuf() for c in cases]
+    wss = [c.dwsbuf() for c in cases]
     for i in range(14):
         for k, c in enumerate(cases):
             if k == 2 and i == 13:
@@ -179,7 +187,7 @@ def test_one_launch_fallback_path(spin, monkeypatch):
     c.two_launch(c.wsbuf(), ref)
     monkeypatch.setenv("OPROJ_FUSED_DECODE_SPIN_LIMIT", spin)
     outs = [c.zbuf() for _ in range(3)]
-    ws = c.wsbuf()
+    ws = c.dwsbuf()
     for z in outs:
         c.one_launch(ws, z)
     monkeypatch.delenv("OPROJ_FUSED_DECODE_SPIN_LIMIT")
@@ -195,7 +203,7 @@ def test_one_launch_graph_replays():
     entry point and new inputs between replays, equals the eager result."""
     c = _Case(450, 64, 16, 8, 1024, F32, B128)
     c.require_one_launch()
-    ws, z = c.wsbuf(), c.zbuf()
+    ws, z = c.dwsbuf(), c.zbuf()
     c.one_launch(ws, z)
     torch.cuda.synchronize()
     ref0 = z.clone()
@@ -223,7 +231,7 @@ def test_one_launch_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(z, z_alt if r % 2 else ref0), r
-        c.one_launch(c.wsbuf(), c.zbuf())  # eager work between replays
+        c.one_launch(c.dwsbuf(), c.zbuf())  # eager work between replays
         torch.cuda.synchronize()
 
 
@@ -247,21 +255,21 @@ def test_one_launch_refuses_shapes_that_do_not_fit():
     z = c.zbuf()
     big = ap.Shape(T=65, n_groups=2, heads_per_group=8, o_lora_rank=128, max_pos=8192)
     with pytest.raises(ap.OprojError) as ei:
-        ap.oproj_fused_decode(big, F32, c.d_o, c.d_pos, c.d_tab, c.d_wq, c.d_ws, B128, c.wsbuf(),
-                              ap.oproj_fused_workspace_bytes(big, 0), z)
+        ap.oproj_fused_decode(big, F32, c.d_o, c.d_pos, c.d_tab, c.d_wq, c.d_ws, B128, c.dwsbuf(),
+                              ap.oproj_fused_decode_workspace_bytes(big), z)
     assert ei.value.status == 2
     # buffers sized for the wide shape, so that nothing would be out of bounds
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     G, R, D = cus // 16 + 1, 1024, 8 * 512  # 16 workgroups per group
     wide = ap.Shape(T=8, n_groups=G, heads_per_group=8, o_lora_rank=R, max_pos=8192)
-    nb = ap.oproj_fused_workspace_bytes(wide, 0)
+    nb = ap.oproj_fused_decode_workspace_bytes(wide)
     o = torch.zeros((8, G * 8, 512), dtype=torch.int16, device=DEV)
     wq = torch.zeros((G * R, D), dtype=torch.uint8, device=DEV)
     wsc = torch.ones((G * R // 128, D // 128), dtype=torch.float32, device=DEV)
     zw = torch.full((8, G, R), 0x7BAD, dtype=torch.int16, device=DEV)
     with pytest.raises(ap.OprojError) as ei:
         ap.oproj_fused_decode(wide, F32, o, c.d_pos, c.d_tab, wq, wsc, B128,
-                              torch.empty(nb, dtype=torch.uint8, device=DEV), nb, zw)
+                              torch.zeros(nb, dtype=torch.uint8, device=DEV), nb, zw)
     assert ei.value.status == 2
     torch.cuda.synchronize()
     assert bool((z == 0x7BAD).all()) and bool((zw == 0x7BAD).all())
@@ -289,4 +297,34 @@ def test_two_launch_path_is_safe_on_concurrent_streams():
     torch.cuda.synchronize()
     for k in range(2):
         for i in range(8):
+            assert torch.equal(outs[k][i], refs[k]), (k, i)
+
+
+def test_one_launch_calls_overlapping_on_two_streams():
+    """Two one-launch calls at a time, on two streams, each with its own
+    workspace (and so its own barrier words): every result equals the
+    single-stream two-launch result, call after call."""
+    cases = [_Case(480, 64, 8, 8, 1024, F32, B128), _Case(481, 48, 4, 8, 1024, P2, B1)]  # 128 + 64 workgroups
+    for c in cases:
+        c.require_one_launch()
+    if sum(c.G * ((c.R + 63) // 64) for c in cases) > torch.cuda.get_device_properties(0).multi_processor_count:
+        pytest.skip("the two grids do not fit on the device together")
+    refs = []
+    for c in cases:
+        z = c.zbuf()
+        c.two_launch(c.wsbuf(), z)
+        refs.append(z)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[c.zbuf() for _ in range(12)] for c in cases]
+    wss = [c.dwsbuf() for c in cases]
+    torch.cuda.synchronize()
+    for i in range(12):
+        for k, c in enumerate(cases):
+            with torch.cuda.stream(streams[k]):
+                ap.oproj_fused_decode(c.shp, c.mode, c.d_o, c.d_pos, c.d_tab, c.d_wq, c.d_ws, c.wblock, wss[k],
+                                      c.dbytes, outs[k][i], stream=streams[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        for i in range(12):
             assert torch.equal(outs[k][i], refs[k]), (k, i)
