@@ -36,6 +36,17 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Size checks of non-negative values that cannot overflow: products and sums
+// saturate at INT64_MAX, which every limit below rejects.
+int64_t mul_sat(int64_t a, int64_t b) {
+    if (a <= 0 || b <= 0) return 0;
+    return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+int64_t add_sat(int64_t a, int64_t b) { return a > INT64_MAX - b ? INT64_MAX : a + b; }
+
+constexpr int64_t kLim32 = int64_t(1) << 32;  // the kernels' 32-bit lane offsets
+constexpr int64_t kLimMem = int64_t(1) << 47;  // larger than any device allocation
+
 // Head geometry and shape checks shared by every entry point.  Mirrors the
 // preconditions fused_inv_rope_fp8_quant asserts (vLLM API page
 // "vllm.models.deepseek_v4.common.ops.fused_inv_rope_fp8_quant"): H = G*hpg,
@@ -53,9 +64,13 @@ oproj_status check_shape(const oproj_shape* s, bool need_rank) {
     if (s->nope_dim != 448 || s->rope_dim != 64 || s->quant_block != 128) return OPROJ_E_MODE;
     const int64_t hpg = s->heads_per_group;
     if (!(hpg == 1 || hpg == 2 || hpg == 4 || hpg % 8 == 0)) return OPROJ_E_MODE;
-    if (s->T > (int64_t(1) << 31) || s->n_groups * hpg > 65536) return OPROJ_E_SHAPE;
-    if (need_rank && (s->o_lora_rank < 64 || s->o_lora_rank % 64 != 0 || s->o_lora_rank > 65536))
+    if (s->T > (int64_t(1) << 31) || s->n_groups > 65536 || hpg > 65536 || s->n_groups * hpg > 65536)
         return OPROJ_E_SHAPE;
+    if (need_rank) {
+        if (s->o_lora_rank < 64 || s->o_lora_rank % 64 != 0 || s->o_lora_rank > 65536) return OPROJ_E_SHAPE;
+        // z [T][G][R] in bf16 must be addressable
+        if (mul_sat(mul_sat(mul_sat(s->T, s->n_groups), s->o_lora_rank), 2) > kLimMem) return OPROJ_E_SHAPE;
+    }
     return OPROJ_OK;
 }
 
@@ -85,6 +100,9 @@ oproj_status check_layout(const oproj_act_layout* l) {
     if (!l) return OPROJ_OK;
     if (l->stride_t < 0 || l->stride_g < 0 || l->s_stride_t < 0 || l->s_stride_g < 0 ||
         l->s_stride_kb < 0)
+        return OPROJ_E_SHAPE;
+    if (l->stride_t > kLimMem || l->stride_g > kLimMem || l->s_stride_t > kLimMem || l->s_stride_g > kLimMem ||
+        l->s_stride_kb > kLimMem)
         return OPROJ_E_SHAPE;
     if (l->stride_t % 16 != 0 || l->stride_g % 16 != 0) return OPROJ_E_ALIGN;
     return OPROJ_OK;
@@ -172,10 +190,14 @@ oproj_status prep_gemm(const oproj_shape* shape, int32_t scale_mode, const void*
     {
         // the kernels address operands as a uniform base plus 32-bit lane offsets
         const oproj::ActLayout l = to_layout(a_layout, shape, scale_mode);
-        const int64_t D = shape->heads_per_group * 512, KB = D / 128, lim = int64_t(1) << 32;
-        const int64_t rows = shape->n_groups * shape->o_lora_rank;
-        if ((shape->T - 1) * l.stride_t + D >= lim || (shape->T - 1) * l.s_stride_t * 4 + 4 >= lim ||
+        const int64_t D = shape->heads_per_group * 512, KB = D / 128, lim = kLim32;
+        const int64_t rows = shape->n_groups * shape->o_lora_rank, T1 = shape->T - 1, G1 = shape->n_groups - 1;
+        if (add_sat(mul_sat(T1, l.stride_t), D) >= lim || add_sat(mul_sat(mul_sat(T1, l.s_stride_t), 4), 4) >= lim ||
             rows * D >= lim || rows * KB * 4 >= lim)
+            return OPROJ_E_SHAPE;
+        // each group's operand base (64-bit) stays inside an addressable range
+        if (mul_sat(G1, l.stride_g) >= kLimMem || add_sat(mul_sat(G1, l.s_stride_g), mul_sat(KB, l.s_stride_kb)) >=
+                                                        kLimMem)
             return OPROJ_E_SHAPE;
     }
     a->T = shape->T;
@@ -254,8 +276,8 @@ oproj_status oproj_dense_bf16_gemm(int64_t M, int64_t N, int64_t K, const void* 
                                    void* y, void* stream) {
     if (M < 0 || N < 1 || K < 64 || K % 64 != 0 || N % 16 != 0) return OPROJ_E_SHAPE;
     // the kernel addresses each operand as a uniform base plus 32-bit lane offsets
-    const int64_t lim = (int64_t)1 << 32;
-    if (M * K * 2 > lim || N * K * 2 > lim) return OPROJ_E_SHAPE;
+    if (mul_sat(mul_sat(M, K), 2) > kLim32 || mul_sat(mul_sat(N, K), 2) > kLim32) return OPROJ_E_SHAPE;
+    if (mul_sat(mul_sat(M, N), 2) > kLimMem) return OPROJ_E_SHAPE;
     if (M == 0) return OPROJ_OK;
     if (!x || !w || !y) return OPROJ_E_NULL;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return OPROJ_E_ALIGN;
@@ -279,7 +301,8 @@ oproj_status bf16_layout(const oproj_shape* s, const oproj_bf16_layout* l, int64
         *sg = D;
         return OPROJ_OK;
     }
-    if (l->stride_t < 0 || l->stride_g < 0) return OPROJ_E_SHAPE;
+    if (l->stride_t < 0 || l->stride_g < 0 || l->stride_t > kLimMem || l->stride_g > kLimMem) return OPROJ_E_SHAPE;
+    if (mul_sat(s->n_groups - 1, l->stride_g) >= kLimMem) return OPROJ_E_SHAPE;
     if (l->stride_t % 8 != 0 || l->stride_g % 8 != 0) return OPROJ_E_ALIGN;
     *st = l->stride_t;
     *sg = l->stride_g;
@@ -325,8 +348,7 @@ oproj_status oproj_grouped_wo_a_bf16(const oproj_shape* shape, const void* x,
     if (!aligned16(x) || !aligned16(w) || !aligned16(z)) return OPROJ_E_ALIGN;
     const int64_t D = shape->heads_per_group * 512, R = shape->o_lora_rank, G = shape->n_groups;
     // the kernel addresses a group's operands as a uniform base plus 32-bit lane offsets
-    const int64_t lim = int64_t(1) << 32;
-    if ((shape->T - 1) * xst * 2 + D * 2 > lim || R * D * 2 > lim) return OPROJ_E_SHAPE;
+    if (add_sat(mul_sat(mul_sat(shape->T - 1, xst), 2), D * 2) > kLim32 || R * D * 2 > kLim32) return OPROJ_E_SHAPE;
     oproj::Bf16GemmArgs a;
     a.G = G;
     a.M = shape->T;
@@ -370,7 +392,9 @@ oproj_status oproj_fused_bf16(const oproj_shape* shape, const void* o, const int
     if ((T - 1) * G * D * 2 + D * 2 > lim || R * D * 2 > lim) return OPROJ_E_SHAPE;
     if (wo_b) {
         const int64_t K = G * R;
-        if (K % 64 != 0 || T * K * 2 > lim || hidden * K * 2 > lim) return OPROJ_E_SHAPE;
+        if (K % 64 != 0 || mul_sat(mul_sat(T, K), 2) > lim || mul_sat(mul_sat(hidden, K), 2) > lim ||
+            mul_sat(mul_sat(T, hidden), 2) > kLimMem)
+            return OPROJ_E_SHAPE;
         if (!aligned16(wo_b)) return OPROJ_E_ALIGN;
     }
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -408,8 +432,10 @@ oproj_status oproj_fused(const oproj_shape* shape, int32_t scale_mode, const voi
                          workspace, workspace_bytes, out, &qa, &ga, &zbuf)) != OPROJ_OK)
         return st;
     if (wo_b) {  // validate a4 before anything is enqueued
-        const int64_t K = shape->n_groups * shape->o_lora_rank, lim = int64_t(1) << 32;
-        if (K % 64 != 0 || shape->T * K * 2 > lim || hidden * K * 2 > lim) return OPROJ_E_SHAPE;
+        const int64_t K = shape->n_groups * shape->o_lora_rank, lim = kLim32;
+        if (K % 64 != 0 || mul_sat(mul_sat(shape->T, K), 2) > lim || mul_sat(mul_sat(hidden, K), 2) > lim ||
+            mul_sat(mul_sat(shape->T, hidden), 2) > kLimMem)
+            return OPROJ_E_SHAPE;
         if (!aligned16(wo_b)) return OPROJ_E_ALIGN;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -465,6 +491,8 @@ const char* oproj_fused_decode_unsupported(const oproj_shape* shape, int32_t sca
 oproj_status oproj_quantize_weight(int64_t rows, int64_t K, int32_t w_block, int32_t scale_mode,
                                    const float* w, void* codes, void* scales, void* stream) {
     if (rows < 0 || K < 128 || K % 128 != 0) return OPROJ_E_SHAPE;
+    // grid: one workgroup per block (rows / block rows, K / 128 <= 65535)
+    if (rows >= (int64_t(1) << 31) || K / 128 > 65535 || mul_sat(rows, K) > kLimMem) return OPROJ_E_SHAPE;
     if (!valid_mode(scale_mode) || !valid_wblock(w_block, scale_mode)) return OPROJ_E_MODE;
     if (w_block == OPROJ_WBLOCK_1x128_UE8M0 && K % 512 != 0) return OPROJ_E_SHAPE;
     if (rows == 0) return OPROJ_OK;
