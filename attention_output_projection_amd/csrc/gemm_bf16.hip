@@ -42,13 +42,23 @@ struct DParams {
     int64_t M, N, K;
     int64_t sx, sy, gx, gw, gy;  // row and group strides, elements
     int64_t G, mtiles, ntiles;   // tiles per group: mtiles x ntiles
-    int nxcd;                    // XCDs of the device (workgroups are dealt to them round-robin)
+    uint32_t tpg;                // mtiles * ntiles
+    uint32_t xcd_per;            // tiles per XCD when the XCD remap applies, else 0
+    int xcd_shift;               // log2 of the XCD count (a power of two) when it applies
 };
 
-// Workgroup id -> tile id such that each XCD runs one contiguous range of tiles.
-__device__ __forceinline__ int64_t xcd_remap_d(int64_t bid, int64_t nblocks, int nxcd) {
-    if (nxcd <= 1 || nblocks % nxcd != 0) return bid;
-    return (bid % nxcd) * (nblocks / nxcd) + bid / nxcd;
+// Workgroup ids are dealt to the XCDs round-robin: map them to tile numbers
+// such that each XCD runs one contiguous range of tiles, and split off the
+// group.  32-bit scalar arithmetic on counts the host prepares.
+struct GroupTile {
+    uint32_t g, id;  // group, tile within the group
+};
+__device__ __forceinline__ GroupTile group_tile(const DParams& p) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t t =
+        p.xcd_per ? (b & ((1u << p.xcd_shift) - 1u)) * p.xcd_per + (b >> p.xcd_shift) : b;
+    const uint32_t g = t / p.tpg;
+    return {g, t - g * p.tpg};
 }
 
 template <int NI>
@@ -60,16 +70,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int wm = wave & 3, wn = wave >> 2;
-    const int64_t per = p.mtiles * p.ntiles;
-    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per, p.nxcd);
-    const int64_t g = gid / per, id = gid - g * per;
+    const GroupTile gt = group_tile(p);
+    const int64_t g = gt.g;
     // band order: BAND M-tiles x all N-tiles, M fastest within the band
-    const int64_t band = id / (BAND * p.ntiles);
-    const int64_t mfirst = band * BAND;
-    const int64_t bh = (p.mtiles - mfirst) < BAND ? (p.mtiles - mfirst) : BAND;
-    const int64_t local = id - band * BAND * p.ntiles;
-    const int64_t mt = mfirst + local % bh, nt = local / bh;
-    const int64_t m0 = mt * BM, n0 = nt * BN;
+    const uint32_t ntl = (uint32_t)p.ntiles, mtl = (uint32_t)p.mtiles;
+    const uint32_t band = gt.id / (BAND * ntl);
+    const uint32_t mfirst = band * BAND;
+    const uint32_t bh = (mtl - mfirst) < BAND ? (mtl - mfirst) : BAND;
+    const uint32_t local = gt.id - band * BAND * ntl;
+    const uint32_t nt = local / bh, mt = mfirst + (local - nt * bh);
+    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
     const int64_t kbytes = p.K * 2, xrow = p.sx * 2;
     const int64_t nstage = kbytes / 128;
 
@@ -219,10 +229,10 @@ __global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) 
     const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row group of the tile
     const bool copier = wave < 2;
-    const int64_t per = p.mtiles * p.ntiles;
-    const int64_t gid = xcd_remap_d(blockIdx.x, p.G * per, p.nxcd);
-    const int64_t g = gid / per, id = gid - g * per;
-    const int64_t m0 = (id / p.ntiles) * XBM, n0 = (id % p.ntiles) * XBN;
+    const GroupTile gt = group_tile(p);
+    const int64_t g = gt.g;
+    const uint32_t mt = gt.id / (uint32_t)p.ntiles, nt = gt.id - mt * (uint32_t)p.ntiles;
+    const int64_t m0 = (int64_t)mt * XBM, n0 = (int64_t)nt * XBN;
     const int64_t kbytes = p.K * 2, xrow = p.sx * 2;
     const int64_t nstep = kbytes / 128;
     const int64_t s0 = nstep * kq / XKS, ns = nstep * (kq + 1) / XKS - s0;
@@ -315,6 +325,22 @@ __global__ __launch_bounds__(XKS * 256) void gemm_bf16_decode_kernel(DParams p) 
     }
 }
 
+// Fills p's tile map for a grid of G x mtiles x ntiles workgroups of `threads`
+// work-items on a device of nx XCDs; false when the grid is beyond one launch
+// (more than 2^32 - 1 work-items in all).
+bool set_tile_map(DParams& p, int threads, int nx) {
+    const int64_t nblocks = p.G * p.mtiles * p.ntiles;
+    if (nblocks < 1 || nblocks > (int64_t)UINT32_MAX / threads) return false;
+    p.tpg = (uint32_t)(p.mtiles * p.ntiles);
+    p.xcd_per = 0;
+    p.xcd_shift = 0;
+    if (nx > 1 && (nx & (nx - 1)) == 0 && nblocks % nx == 0) {
+        p.xcd_shift = __builtin_ctz((unsigned)nx);
+        p.xcd_per = (uint32_t)(nblocks / nx);
+    }
+    return true;
+}
+
 }  // namespace
 
 hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
@@ -332,12 +358,12 @@ hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
     p.gy = a.gy;
     p.G = a.G;
     const DeviceInfo dev = current_device_info();
-    p.nxcd = dev.xcds;
     if (a.M <= 128) {  // few tokens: 64x64 tiles, K split over two wave groups
         p.mtiles = (a.M + XBM - 1) / XBM;
         p.ntiles = (a.N + XBN - 1) / XBN;
-        hipLaunchKernelGGL(gemm_bf16_decode_kernel, dim3((unsigned)(a.G * p.mtiles * p.ntiles)),
-                           dim3(XKS * 256), 0, stream, p);
+        if (!set_tile_map(p, XKS * 256, dev.xcds)) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(gemm_bf16_decode_kernel, dim3(p.tpg * (uint32_t)p.G), dim3(XKS * 256), 0,
+                           stream, p);
         return hipGetLastError();
     }
     p.mtiles = (a.M + BM - 1) / BM;
@@ -353,7 +379,8 @@ hipError_t launch_bf16_gemm(const Bf16GemmArgs& a, hipStream_t stream) {
     else if (fill(t224) > fill(t256) + 0.02)
         ni = 7;
     p.ntiles = (a.N + 32 * ni - 1) / (32 * ni);
-    const dim3 grid((unsigned)(a.G * p.mtiles * p.ntiles)), block(NW * 64);
+    if (!set_tile_map(p, NW * 64, dev.xcds)) return hipErrorInvalidConfiguration;
+    const dim3 grid(p.tpg * (uint32_t)p.G), block(NW * 64);
     if (ni == 2)
         hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, block, 0, stream, p);
     else if (ni == 7)

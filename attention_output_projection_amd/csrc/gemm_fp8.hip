@@ -69,7 +69,10 @@ struct GParams {
     int e8;       // activation scales are packed UE8M0 words (block scaled MFMA only)
     int spin = 0;  // one-launch path: polls of a group barrier before the fallback
     uint64_t* sync = nullptr;  // one-launch path: the groups' barrier words (caller's workspace)
-    int nxcd = 1;  // XCDs of the device (workgroups are dealt to them round-robin)
+    uint32_t tpg = 1;      // tiles per group (mtiles * ntiles)
+    uint32_t nt32 = 1;     // ntiles
+    uint32_t xcd_per = 0;  // tiles per XCD when the XCD remap applies, else 0
+    int xcd_shift = 0;     // log2 of the XCD count (a power of two) when it applies
     int pfd = 0;   // tile kernels: L2 prefetch distance in K-blocks (0: none)
 };
 
@@ -91,10 +94,19 @@ __device__ __forceinline__ v4f mfma_fp8_mx(const v8i& a, const v8i& b, const v4f
 }
 
 // Workgroup ids are dealt to the XCDs round-robin: remap them so that each XCD
-// runs one contiguous range of tiles (the same group).
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks, int nxcd) {
-    if (nxcd <= 1 || nblocks % nxcd != 0) return bid;
-    return (bid % nxcd) * (nblocks / nxcd) + bid / nxcd;
+// runs one contiguous range of tiles (the same group), then split the tile
+// number into (group, M-tile, N-tile).  The host prepares the shift and the
+// counts (set_tile_map), so this is a handful of 32-bit scalar operations.
+struct TileCoord {
+    int64_t g, mt, nt;
+};
+__device__ __forceinline__ TileCoord tile_coord(const GParams& p) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t t =
+        p.xcd_per ? (b & ((1u << p.xcd_shift) - 1u)) * p.xcd_per + (b >> p.xcd_shift) : b;
+    const uint32_t g = t / p.tpg, r = t - g * p.tpg;
+    const uint32_t mt = r / p.nt32;
+    return {(int64_t)g, (int64_t)mt, (int64_t)(r - mt * p.nt32)};
 }
 
 __device__ __forceinline__ int64_t wscale_index(const GParams& p, int64_t wrow, int64_t kb) {
@@ -149,11 +161,8 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int wm = wave & 1, wn = wave >> 1;
-    const int64_t nblocks = p.G * p.mtiles * p.ntiles;
-    const int64_t tile = xcd_remap(blockIdx.x, nblocks, p.nxcd);
-    const int64_t g = tile / (p.mtiles * p.ntiles);
-    const int64_t mt = (tile / p.ntiles) % p.mtiles;
-    const int64_t nt = tile % p.ntiles;
+    const TileCoord tc = tile_coord(p);
+    const int64_t g = tc.g, mt = tc.mt, nt = tc.nt;
     const int64_t m0 = mt * TBM, n0 = nt * TBN;
 
     // ---- copy plan.  Copying wave c (0-3) moves activation rows 64c..64c+63
@@ -373,10 +382,10 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 // of the global loads (global_load_lds: no staging registers).  The eight
 // waves form DKS K-groups of four; each K-group walks its share of the
 // K-blocks through its own ring of DNS stages, DNS-1 of them in flight, with
-// one s_waitcnt + barrier per K-block.  In a K-group, waves 0-1 issue the
-// copies (a copy waits at issue while the CU's memory pipeline is full) and
-// waves 2-3 only compute.  Rows are 128 bytes with the 16-byte pieces
-// XOR-swizzled, which makes the fragment reads conflict-free.  For the MFMAs
+// one s_waitcnt + barrier per K-block.  Every wave of a K-group issues a
+// quarter of the copies (the one-launch path: waves 0-1 half each).  Rows
+// are 128 bytes with the 16-byte pieces XOR-swizzled, which makes the
+// fragment reads conflict-free.  For the MFMAs
 // the waves of a K-group split M: wave w owns token rows 16w..16w+15 against
 // all 64 columns (one activation and four weight fragments per K-block, a
 // third less LDS reading than splitting N); the K-groups' partial tiles are
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 #endif
 constexpr int DBM = 64, DBN = 64, DNS = OPROJ_DEC_DNS, DKS = OPROJ_DEC_DKS;
 constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
-constexpr int DVM = 9;  // copy instructions per copying wave per stage
+constexpr int DVM = 9;  // one-launch path: copy instructions per copying wave per stage
 constexpr int DPROW = DBN + 4;  // fp32 per row of an epilogue partial tile (pad against bank conflicts)
 static_assert(DKS * DBM * DPROW * 4 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
 
@@ -448,36 +457,42 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     const int tid = threadIdx.x, lane = tid & 63;
     const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group within the tile
-    const bool copier = wave < 2;
-    const int64_t nblocks = p.G * p.mtiles * p.ntiles;
-    const int64_t tile = xcd_remap(blockIdx.x, nblocks, p.nxcd);
-    const int64_t g = tile / (p.mtiles * p.ntiles);
-    const int64_t mt = (tile / p.ntiles) % p.mtiles;
-    const int64_t nt = tile % p.ntiles;
+    // Copying waves of the K-group: all four on the plain path (one wave
+    // issues a DMA copy only about every hundred cycles, so two waves' nine
+    // copies per K-block took about half of each step), waves 0-1 on the
+    // one-launch path, whose prologue waits count that plan.
+    constexpr int CW = QCH == 0 ? 4 : 2;
+    constexpr int CR = DBM / CW;  // rows of each slab per copying wave
+    constexpr int CI = CR / 8;    // copy instructions per slab per copying wave
+    const bool copier = wave < CW;
+    const bool scaler = wave < 2;  // waves 0-1 also gather the scales
+    static_assert(QCH == 0 || 2 * CI + 1 == DVM, "the one-launch waits count DVM copies per step");
+    const TileCoord tc = tile_coord(p);
+    const int64_t g = tc.g, mt = tc.mt, nt = tc.nt;
     const int64_t m0 = mt * DBM, n0 = nt * DBN;
     // this K-group's K-blocks: [kb0, kb0 + nkb)
     const int64_t kb0 = p.KB * kq / DKS;
     const int64_t nkb = p.KB * (kq + 1) / DKS - kb0;
 
-    // ---- copy plan.  Copying wave c (0-1): activation rows 32c..32c+31 and
-    // weight rows 32c..32c+31 (8 rows of 128 bytes per instruction), and one
-    // scale gather (lanes 0-31: activation scales of tokens 32c+l; lanes
-    // 32-63: weight scales of columns 32c+l-32).  Sources are uniform bases
-    // plus 32-bit lane offsets.
+    // ---- copy plan.  Copying wave c: activation rows CR*c..CR*c+CR-1 and the
+    // same weight rows (8 rows of 128 bytes per instruction); waves c = 0-1
+    // also make one scale gather (lanes 0-31: activation scales of tokens
+    // 32c+l; lanes 32-63: weight scales of columns 32c+l-32).  Sources are
+    // uniform bases plus 32-bit lane offsets.
     const uint8_t* abase = p.a + g * p.sg;
     const uint8_t* wbase = p.w + g * p.R * p.D;
-    uint32_t off[8];
+    uint32_t off[2 * CI];
     if (copier) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 32 * wave + 8 * j + (lane >> 3);
+        for (int j = 0; j < CI; ++j) {
+            const int row = CR * wave + 8 * j + (lane >> 3);
             const int piece = (lane & 7) ^ swz(row);
             int64_t m = m0 + row;
             m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
             off[j] = (uint32_t)(m * p.st + piece * 16);
             int64_t n = n0 + row;
             n = n < p.R ? n : p.R - 1;
-            off[4 + j] = (uint32_t)(n * p.D + piece * 16);
+            off[CI + j] = (uint32_t)(n * p.D + piece * 16);
         }
     }
     // the scale gather mixes two sources across lanes: 64-bit lane addresses
@@ -498,24 +513,24 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         kshl = p.wkshift;
     }
     const uint32_t ring0 = lds_offset(&ring[kq][0][0]);
-    // step i's copies: the activation slab and the scales (5 instructions),
-    // the weight slab (4)
+    // step i's copies: the activation slab and the scales (CI + 1
+    // instructions on waves 0-1, CI on the others), the weight slab (CI)
     auto issue_a = [&](int64_t i, int slot) __attribute__((always_inline)) {
         const int64_t kb = kb0 + i;
         const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16s(abase + kb * 128, off[j], st + (32 * wave + 8 * j) * 128);
-        dma4(ssrc + (kb >> kshl) * sstep, st + 16384 + 256 * wave);
+        for (int j = 0; j < CI; ++j) dma16s(abase + kb * 128, off[j], st + (CR * wave + 8 * j) * 128);
+        if (scaler) dma4(ssrc + (kb >> kshl) * sstep, st + 16384 + 256 * wave);
     };
     auto issue_w = [&](int64_t i, int slot) __attribute__((always_inline)) {
         const int64_t kb = kb0 + i;
         const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < CI; ++j) {
             if (OPROJ_DEC_W_NT)
-                dma16s_nt(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
+                dma16s_nt(wbase + kb * 128, off[CI + j], st + 8192 + (CR * wave + 8 * j) * 128);
             else
-                dma16s(wbase + kb * 128, off[4 + j], st + 8192 + (32 * wave + 8 * j) * 128);
+                dma16s(wbase + kb * 128, off[CI + j], st + 8192 + (CR * wave + 8 * j) * 128);
         }
     };
     auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
@@ -599,8 +614,10 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
                 if (i == 0) wait_vmcnt<5 * (DNS - 2)>();
                 else if (i == 1) wait_vmcnt<5 * (DNS - 3) + DVM>();
                 else wait_vmcnt<5 * (DNS - 4 > 0 ? DNS - 4 : 0) + 2 * DVM>();
+            } else if (scaler) {
+                wait_ahead<DNS - 2, 2 * CI + 1>(nkb - 1 - i);
             } else {
-                wait_ahead<DNS - 2, DVM>(nkb - 1 - i);
+                wait_ahead<DNS - 2, 2 * CI>(nkb - 1 - i);
             }
         }
         __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence)
@@ -689,8 +706,26 @@ __global__ __launch_bounds__(DKS * 256) void fused_decode_kernel(GParams p, rq::
     decode_tile<MX, W1, QCH>(p, ring, q);
 }
 
+// Fills p's tile map for a grid of G x mtiles x ntiles workgroups of `threads`
+// work-items; false when the grid is beyond one launch (more than 2^32 - 1
+// work-items in all).
+bool set_tile_map(GParams& p, int threads) {
+    const int64_t nblocks = p.G * p.mtiles * p.ntiles;
+    if (nblocks < 1 || nblocks > (int64_t)UINT32_MAX / threads) return false;
+    p.tpg = (uint32_t)(p.mtiles * p.ntiles);
+    p.nt32 = (uint32_t)p.ntiles;
+    p.xcd_per = 0;
+    p.xcd_shift = 0;
+    const int nx = current_device_info().xcds;
+    if (nx > 1 && (nx & (nx - 1)) == 0 && nblocks % nx == 0) {
+        p.xcd_shift = __builtin_ctz((unsigned)nx);
+        p.xcd_per = (uint32_t)(nblocks / nx);
+    }
+    return true;
+}
+
 void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.G * p.mtiles * p.ntiles)), block(DKS * 256);
+    const dim3 grid(p.tpg * (uint32_t)p.G), block(DKS * 256);
     if (mx) {
         if (w1)
             hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, true>), grid, block, 0, stream, p);
@@ -717,11 +752,7 @@ const char* fused_decode_unfit(int64_t T, int64_t G, int64_t hpg, int64_t R) {
     const int ch = rq::heads_per_item(hpg);
     if (ch != 2 && ch != 4) return "heads_per_group is neither 2 nor a multiple of 4";
     if (hpg * 512 / 128 / DKS < DNS) return "head dimension too short for the copy pipeline";
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return "no device to query";
-    if (G * ((R + DBN - 1) / DBN) > cus)
+    if (G * ((R + DBN - 1) / DBN) > current_device_info().cus)
         return "more workgroups (n_groups x o_lora_rank / 64) than compute units";
     return nullptr;
 }
@@ -757,7 +788,7 @@ hipError_t launch_fused_decode(const RopeQuantArgs& qa, const GroupedGemmArgs& a
     p.kbw = a.w_e8m0 ? KB / 4 : KB;
     p.mtiles = 1;
     p.ntiles = ntiles;
-    p.nxcd = current_device_info().xcds;
+    if (!set_tile_map(p, DKS * 256)) return hipErrorInvalidConfiguration;
     p.sync = sync;
     // OPROJ_FUSED_DECODE_SPIN_LIMIT (diagnostics and tests) lowers the polls a
     // workgroup makes before it quantises its whole group itself; 0 sends every
@@ -807,17 +838,18 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.kbw = a.w_e8m0 ? p.KB / 4 : p.KB;
     p.e8 = a.a_e8m0;
     p.kshift = a.a_e8m0 ? 2 : 0;
-    p.nxcd = current_device_info().xcds;
     // decode kernel for few tokens (the weight stream dominates), tile kernel otherwise
     const bool decode = a.T <= 128;
     if (decode) {
         p.mtiles = (a.T + DBM - 1) / DBM;
         p.ntiles = (a.R + DBN - 1) / DBN;
+        if (!set_tile_map(p, DKS * 256)) return hipErrorInvalidConfiguration;
         launch_decode(p, a.mx != 0, a.w_1x128 != 0, stream);
     } else {
         p.mtiles = (a.T + TBM - 1) / TBM;
         p.ntiles = (a.R + TBN - 1) / TBN;
-        const dim3 grid((unsigned)(p.G * p.mtiles * p.ntiles));
+        if (!set_tile_map(p, TNW * 64)) return hipErrorInvalidConfiguration;
+        const dim3 grid(p.tpg * (uint32_t)p.G);
         p.pfd = kTilePrefetch;
         if (a.mx) {
             if (a.w_1x128)
