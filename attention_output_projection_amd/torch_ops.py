@@ -158,7 +158,8 @@ def deep_gemm_fp8_o_proj(o: torch.Tensor, positions: torch.Tensor, cos_sin_cache
                          one_launch: bool = False) -> torch.Tensor:
     """The whole path on bf16 o [T, H, 512]: y = wo_b(z.flatten(1)) bf16
     [T, hidden] when wo_b ([hidden, G*R] bf16) is given, else z bf16 [T, G, R].
-    one_launch takes oproj_fused_decode (steps a1-a3 in one kernel) when it
+    one_launch (experimental, off by default: slower than the two launches on
+    MI355X) takes oproj_fused_decode (steps a1-a3 in one kernel) when it
     supports the shape and wo_b is None, and oproj_fused otherwise."""
     _need(isinstance(o, torch.Tensor) and o.dim() == 3, "o must be a [T, H, 512] tensor")
     T = o.shape[0]

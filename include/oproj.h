@@ -275,7 +275,11 @@ oproj_status oproj_fused_noalloc(const oproj_shape* shape, int32_t scale_mode, c
                                  const void* w_scales, int32_t w_block, const void* wo_b, int64_t hidden,
                                  void* out, void* stream);
 
-/* Steps a1 + a2 + a3 of oproj_fused (wo_b == NULL) in ONE kernel launch, for
+/* EXPERIMENTAL, opt-in: on MI355X this one-launch form has measured slower
+ * than oproj_fused's two launches (about 24 us against 22 us per step at
+ * T = 64, 16 groups x 8 heads, o_lora_rank 1024), so oproj_fused does not
+ * use it.
+ * Steps a1 + a2 + a3 of oproj_fused (wo_b == NULL) in ONE kernel launch, for
  * decode-sized batches, where the launch and the quantisation round trip sit
  * on the per-token critical path ([SGL] the wo_a decode path; [FUSED] feeds
  * the grouped GEMM directly).  Each workgroup first quantises its share of
