@@ -86,3 +86,36 @@ def test_noalloc_t0_and_invalid_shape():
         ap.oproj_fused_noalloc(ap.Shape(T=4, n_groups=2, heads_per_group=2, o_lora_rank=10, max_pos=16),
                                0, None, None, None, None, None, 0, None, 0, None)
     assert e.value.status == 2
+
+
+def test_noalloc_replays_under_graph_capture():
+    """The callers it is for: a HIP graph holding the call (captured after one
+    eager call, which looks the array up), replayed four times with eager work
+    between the replays, among it a call on another input that overwrites the
+    array; every replay equals the eager result bit for bit."""
+    args, shape_out = _case(wl.WORKLOADS["decode"], 0)
+    other, other_out = _case(wl.Workload(98, "other", T=9, n_groups=2, heads_per_group=8, o_lora_rank=128,
+                                         max_pos=4096, positions="uniform"), 0)
+    ref = torch.empty(shape_out, dtype=torch.int16, device=DEV)
+    ap.oproj_fused_noalloc(*args, ref)
+    torch.cuda.synchronize()
+    out = torch.full(shape_out, 0x7BAD, dtype=torch.int16, device=DEV)
+    junk = torch.empty(other_out, dtype=torch.int16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            ap.oproj_fused_noalloc(*args, out)
+    torch.cuda.synchronize()
+    try:
+        for rep in range(4):
+            out.fill_(0x7BAD)                      # a fill kernel, eager
+            ap.oproj_fused_noalloc(*other, junk)   # the array now holds another call's data
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"replay {rep} differs"
+    finally:
+        torch.cuda.synchronize()
+        g.reset()
