@@ -129,11 +129,15 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 // the block's scales), DMA-copied into a double-buffered LDS ring with
 // XOR-swizzled 128-byte rows; one s_waitcnt + bare barrier per K-block.
 //
-// Waves 0-3 issue all copies of a stage (18 each, right after the barrier);
-// waves 4-7 only compute.  A copy waits at issue while the CU's memory
-// pipeline is full, which at these tile sizes lasts longer than a K-block's
-// MFMAs; a copying wave therefore starts its MFMAs late, and its SIMD partner
-// (a wave that never copies) keeps the matrix core busy meanwhile.
+// Waves 0-3 issue all copies of a stage (18 each, right after the barrier,
+// which leaves the copies a whole K-block to land in a two-stage ring);
+// waves 4-7 only compute.  A copy waits at issue until the CU's DMA path
+// (about 64 bytes per clock) accepts it, so a copying wave spends roughly half
+// of a K-block's MFMA time issuing and starts its MFMAs late; its SIMD partner
+// (a wave that never copies) keeps the matrix core busy meanwhile.  Copies
+// placed among the MFMAs instead, by these waves or by all eight, delay the
+// MFMAs of every wave that issues them and leave the late ones less than a
+// K-block to land.
 //
 // The CU's memory pipeline holds a fixed number of outstanding lines, so the
 // copy rate is set by their latency: lines that miss in L2 cost several times
