@@ -15,10 +15,12 @@
 //
 // Block scales:
 //  * fp32 recipe: each 128-deep MFMA writes a fresh fp32 partial P, folded
-//    into the accumulator as acc = fma(P, sa[row]*sw[col], acc) (sw is one
-//    value per 128 output columns in the 128x128 weight recipe, so the
-//    product sa*sw is formed once per row and K-block and reused across the
-//    wave's column subtiles);
+//    into the accumulator as acc = fma(P, sa[token]*sw[row], acc).  In the
+//    128x128 weight recipe sw is one value per 128 weight rows, and the tile
+//    kernel makes the weights the MFMA's row operand: a lane's four partials
+//    then belong to one token, and one product sa*sw serves all of them
+//    (four fma and a quarter multiply per MFMA, which the SIMD overlaps with
+//    the matrix core; five per MFMA measured 2-3% slower);
 //  * pow2 recipe (both scale sets are powers of two): the block-scaled MFMA
 //    v_mfma_scale_f32_16x16x128_f8f6f4 applies the E8M0 exponents of sa and
 //    sw in the matrix core and accumulates directly; no VALU work per block.
@@ -251,7 +253,6 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     const int p0 = 2 * (lane >> 4);
     const int lo_off = frow * 128 + 16 * (p0 ^ swz(frow));
     const int hi_off = frow * 128 + 16 * ((p0 + 1) ^ swz(frow));
-    const int sa_off = 4 * (128 * wm + 4 * (lane >> 4));  // activation scales of the lane's rows
     auto frag = [&](const uint8_t* base) __attribute__((always_inline)) {
         const uint4 lo = *reinterpret_cast<const uint4*>(base + lo_off);
         const uint4 hi = *reinterpret_cast<const uint4*>(base + hi_off);
@@ -261,16 +262,27 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
     // fp32 recipe: the partials of the subtile issued last and their scale
     // factors, folded into the accumulators one subtile later (the last
     // subtile of a K-block across the barrier into the next K-block), so that
-    // the matrix core has the next subtile's MFMAs to run while they wait
+    // the matrix core has the next subtile's MFMAs to run while they wait.
+    // With 128x128 weight blocks the weights are the MFMA's 16-row operand
+    // and the tokens its 16 columns: a lane's four partials are then four
+    // weight rows of one token and share one factor sa[token] * sw[block],
+    // one multiply per subtile instead of one per row.  With per-row weight
+    // scales the tokens stay the row operand (each partial has its own
+    // factor either way, and this form holds fewer of them).
     v4f pend[4];
-    float psa[4] = {0.f, 0.f, 0.f, 0.f}, psw[4] = {0.f, 0.f, 0.f, 0.f};  // their row and column scales
+    float ps = 0.f;                                                      // 128x128 blocks
+    float psa[4] = {0.f, 0.f, 0.f, 0.f}, psw[4] = {0.f, 0.f, 0.f, 0.f};  // per-row weight scales
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) pend[ni] = v4f{0.f, 0.f, 0.f, 0.f};
     auto fold = [&](int mi, int ni) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mi][ni][i] = __builtin_fmaf(pend[ni][i], psa[i] * psw[ni], acc[mi][ni][i]);
+        for (int i = 0; i < 4; ++i)
+            acc[mi][ni][i] = __builtin_fmaf(pend[ni][i], W1 ? psa[i] * psw[ni] : ps, acc[mi][ni][i]);
     };
 
+    // not unrolled or peeled: a peeled first K-block is a second copy of the
+    // loop body, and that copy spills
+#pragma clang loop unroll(disable)
     for (int64_t kb = 0; kb < p.KB; ++kb) {
         // this wave's copies of stage kb have landed (a prefetch issued after
         // them may still be in flight: loads complete in order)
@@ -295,7 +307,6 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         // the activation fragment of subtile mi+1 (and its scales) is read
         // from LDS while the MFMAs of subtile mi run; each subtile's four MFMAs
         // are issued before their partials are folded into the accumulators
-        const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + sa_off;
         v8i afn = frag(sta);
         if constexpr (MX) {
             int eb[4];
@@ -313,17 +324,12 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
             }
-        } else {
+        } else if constexpr (W1) {
             float swv[4];
-            if constexpr (W1) {
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
-            } else {
-                const float sws = scw[64 * wn];  // one weight scale per 64-column span
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) swv[ni] = sws;
-            }
-            float4 tn = *reinterpret_cast<const float4*>(sab);
+            for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
+            const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * (128 * wm + 4 * (lane >> 4));
+            float4 tn = *reinterpret_cast<const float4*>(sab);  // the scales of the lane's four rows
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
                 const v8i af = afn;
@@ -342,6 +348,25 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) psa[i] = sa4[i];
             }
+        } else {
+            const float sws = scw[64 * wn];  // one weight scale per 64-row span
+            float san = sca[128 * wm + frow];  // the lane's token of subtile 0
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const v8i af = afn;
+                const float sa = san;
+                if (mi < 7) {
+                    afn = frag(sta + (mi + 1) * 2048);
+                    san = sca[128 * wm + 16 * (mi + 1) + frow];
+                }
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const v4f q = mfma_fp8(bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f});  // rows: weights
+                    fold(mi == 0 ? 7 : mi - 1, ni);
+                    pend[ni] = q;
+                }
+                ps = sa * sws;
+            }
         }
     }
     if constexpr (!MX) {
@@ -358,13 +383,22 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < 4; ++ni) {
+            if constexpr (MX || W1) {  // a lane holds one column of four rows
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
-                const int c = 64 * wn + 16 * ni + frow;
-                stile[r * TEROW + c] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
+                    const int c = 64 * wn + 16 * ni + frow;
+                    stile[r * TEROW + c] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
+                }
+            } else {  // a lane holds four adjacent columns of one row: one 8-byte write
+                const int r = 128 * wm + 16 * mi + frow;
+                const int c = 64 * wn + 16 * ni + 4 * (lane >> 4);
+                const uint2 v = {f32_to_bf16_bits(acc[mi][ni][0]) | (f32_to_bf16_bits(acc[mi][ni][1]) << 16),
+                                 f32_to_bf16_bits(acc[mi][ni][2]) | (f32_to_bf16_bits(acc[mi][ni][3]) << 16)};
+                *reinterpret_cast<uint2*>(stile + r * TEROW + c) = v;
             }
+        }
     __syncthreads();
     // 32 lanes per row, 16 bytes each; a wave stores 2 rows per instruction
     const int half = lane >> 5, l32 = lane & 31;
