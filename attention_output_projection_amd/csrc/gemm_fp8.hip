@@ -40,6 +40,7 @@
 // each workgroup quantises its share of its group into a workspace, the
 // group's workgroups meet at a barrier of their own, then each runs its tile.
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -131,15 +132,17 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 // the block's scales), DMA-copied into a double-buffered LDS ring with
 // XOR-swizzled 128-byte rows; one s_waitcnt + bare barrier per K-block.
 //
-// Waves 0-3 issue all copies of a stage (18 each, right after the barrier,
-// which leaves the copies a whole K-block to land in a two-stage ring);
-// waves 4-7 only compute.  A copy waits at issue until the CU's DMA path
-// (about 64 bytes per clock) accepts it, so a copying wave spends roughly half
-// of a K-block's MFMA time issuing and starts its MFMAs late; its SIMD partner
-// (a wave that never copies) keeps the matrix core busy meanwhile.  Copies
-// placed among the MFMAs instead, by these waves or by all eight, delay the
-// MFMAs of every wave that issues them and leave the late ones less than a
-// K-block to land.
+// Waves 0-3 issue all copies of a stage (18 each), one per SIMD; waves 4-7
+// only compute.  A copy waits at issue until the CU's DMA path (about 64
+// bytes per clock) accepts it, so a copying wave is held while the path
+// drains the copies ahead of its own, and starts its MFMAs late; its SIMD
+// partner (a wave that never copies) keeps the matrix core busy meanwhile.
+// The copies go in two bursts of half the stage: waves 0-1 right after the
+// barrier, waves 2-3 in the middle of the K-block, which still leaves their
+// copies half a K-block to land.  Each burst holds its waves about half as
+// long as one burst of all four.  Copies spread thinner (four bursts, or a
+// few copies after every subtile, or by all eight waves) delay more MFMAs
+// than they free, or land too late.
 //
 // The CU's memory pipeline holds a fixed number of outstanding lines, so the
 // copy rate is set by their latency: lines that miss in L2 cost several times
@@ -157,6 +160,8 @@ constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
 constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
 constexpr int TEROW = TBN + 8;      // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
 constexpr int kTilePrefetch = 2;    // L2 prefetch distance in K-blocks (measured best of 2, 3, 4, 6)
+constexpr int kCopyTop = 0, kCopyMid = 1, kComputeOnly = 2;  // wave roles in the K loop
+constexpr int kMidSubtile = 4;  // waves 2-3 copy before this subtile's MFMAs (measured best of 2, 3, 4, 6)
 static_assert(TBM * TEROW * 2 <= TNS * TSTAGE, "the epilogue tile fits in the ring");
 
 template <bool MX, bool W1>
@@ -280,95 +285,120 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
             acc[mi][ni][i] = __builtin_fmaf(pend[ni][i], W1 ? psa[i] * psw[ni] : ps, acc[mi][ni][i]);
     };
 
-    // not unrolled or peeled: a peeled first K-block is a second copy of the
-    // loop body, and that copy spills
+    // The K loop, instantiated per wave role so that no branch sits among the
+    // MFMAs: waves 0-1 copy their half of a stage right after the barrier
+    // (and issue the L2 prefetch), waves 2-3 after subtile kMidSubtile-1's
+    // MFMAs, waves 4-7 only compute.  Two half-size bursts on the DMA path
+    // hold each copying wave about half as long as one burst of all four.
+    // Not unrolled or peeled: a peeled first K-block is a second copy of the
+    // loop body, and that copy spills.
+    auto kloop = [&](auto role) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role)::value;
 #pragma clang loop unroll(disable)
-    for (int64_t kb = 0; kb < p.KB; ++kb) {
-        // this wave's copies of stage kb have landed (a prefetch issued after
-        // them may still be in flight: loads complete in order)
-        if (copier) {
-            if (pf && kb > 0 && kb + p.pfd < p.KB) wait_vmcnt<1>();
-            else wait_vmcnt<0>();
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kb-1 are done
-        __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
-        if (copier) {
-            issue(kb + 1, (int)((kb + 1) & 1));
-            if (pf) prefetch(kb + 1);
-        }
-        const uint8_t* st = ring[kb & 1];
-        const uint8_t* sta = st + TSA + 128 * wm * 128;
-        const uint8_t* stb = st + TSB + 64 * wn * 128;
-        const float* sca = reinterpret_cast<const float*>(st + TSS);
-        const float* scw = reinterpret_cast<const float*>(st + TSW);
-        v8i bfr[4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) bfr[ni] = frag(stb + ni * 2048);
-        // the activation fragment of subtile mi+1 (and its scales) is read
-        // from LDS while the MFMAs of subtile mi run; each subtile's four MFMAs
-        // are issued before their partials are folded into the accumulators
-        v8i afn = frag(sta);
-        if constexpr (MX) {
-            int eb[4];
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) eb[ni] = w_e8m0(p, __float_as_uint(scw[64 * wn + 16 * ni + frow]), kb);
-            float san = sca[128 * wm + frow];
-#pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = afn;
-                const int ea = act_e8m0(p, __float_as_uint(san), kb);
-                if (mi < 7) {
-                    afn = frag(sta + (mi + 1) * 2048);
-                    san = sca[128 * wm + 16 * (mi + 1) + frow];
-                }
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
+        for (int64_t kb = 0; kb < p.KB; ++kb) {
+            // this wave's copies of stage kb have landed (a prefetch issued
+            // after them may still be in flight: loads complete in order)
+            if constexpr (ROLE == kCopyTop) {
+                if (pf && kb > 0 && kb + p.pfd < p.KB) wait_vmcnt<1>();
+                else wait_vmcnt<0>();
+            } else if constexpr (ROLE == kCopyMid) {
+                wait_vmcnt<0>();
             }
-        } else if constexpr (W1) {
-            float swv[4];
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
-            const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * (128 * wm + 4 * (lane >> 4));
-            float4 tn = *reinterpret_cast<const float4*>(sab);  // the scales of the lane's four rows
-#pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = afn;
-                const float sa4[4] = {tn.x, tn.y, tn.z, tn.w};
-                if (mi < 7) {
-                    afn = frag(sta + (mi + 1) * 2048);
-                    tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
-                }
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const v4f q = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
-                    fold(mi == 0 ? 7 : mi - 1, ni);
-                    pend[ni] = q;
-                    if (mi == 0) psw[ni] = swv[ni];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) psa[i] = sa4[i];
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kb-1 are done
+            __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
+            if constexpr (ROLE == kCopyTop) {
+                issue(kb + 1, (int)((kb + 1) & 1));
+                if (pf) prefetch(kb + 1);
             }
-        } else {
-            const float sws = scw[64 * wn];  // one weight scale per 64-row span
-            float san = sca[128 * wm + frow];  // the lane's token of subtile 0
+            const uint8_t* st = ring[kb & 1];
+            const uint8_t* sta = st + TSA + 128 * wm * 128;
+            const uint8_t* stb = st + TSB + 64 * wn * 128;
+            const float* sca = reinterpret_cast<const float*>(st + TSS);
+            const float* scw = reinterpret_cast<const float*>(st + TSW);
+            v8i bfr[4];
 #pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = afn;
-                const float sa = san;
-                if (mi < 7) {
-                    afn = frag(sta + (mi + 1) * 2048);
-                    san = sca[128 * wm + 16 * (mi + 1) + frow];
-                }
+            for (int ni = 0; ni < 4; ++ni) bfr[ni] = frag(stb + ni * 2048);
+            // the activation fragment of subtile mi+1 (and its scales) is read
+            // from LDS while the MFMAs of subtile mi run; each subtile's four
+            // MFMAs are issued before their partials are folded into the
+            // accumulators
+            v8i afn = frag(sta);
+            if constexpr (MX) {
+                int eb[4];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const v4f q = mfma_fp8(bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f});  // rows: weights
-                    fold(mi == 0 ? 7 : mi - 1, ni);
-                    pend[ni] = q;
+                for (int ni = 0; ni < 4; ++ni)
+                    eb[ni] = w_e8m0(p, __float_as_uint(scw[64 * wn + 16 * ni + frow]), kb);
+                float san = sca[128 * wm + frow];
+#pragma unroll
+                for (int mi = 0; mi < 8; ++mi) {
+                    if constexpr (ROLE == kCopyMid) {
+                        if (mi == kMidSubtile) issue(kb + 1, (int)((kb + 1) & 1));
+                    }
+                    const v8i af = afn;
+                    const int ea = act_e8m0(p, __float_as_uint(san), kb);
+                    if (mi < 7) {
+                        afn = frag(sta + (mi + 1) * 2048);
+                        san = sca[128 * wm + 16 * (mi + 1) + frow];
+                    }
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
                 }
-                ps = sa * sws;
+            } else if constexpr (W1) {
+                float swv[4];
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
+                const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * (128 * wm + 4 * (lane >> 4));
+                float4 tn = *reinterpret_cast<const float4*>(sab);  // the scales of the lane's four rows
+#pragma unroll
+                for (int mi = 0; mi < 8; ++mi) {
+                    if constexpr (ROLE == kCopyMid) {
+                        if (mi == kMidSubtile) issue(kb + 1, (int)((kb + 1) & 1));
+                    }
+                    const v8i af = afn;
+                    const float sa4[4] = {tn.x, tn.y, tn.z, tn.w};
+                    if (mi < 7) {
+                        afn = frag(sta + (mi + 1) * 2048);
+                        tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
+                    }
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const v4f q = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+                        fold(mi == 0 ? 7 : mi - 1, ni);
+                        pend[ni] = q;
+                        if (mi == 0) psw[ni] = swv[ni];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) psa[i] = sa4[i];
+                }
+            } else {
+                const float sws = scw[64 * wn];  // one weight scale per 64-row span
+                float san = sca[128 * wm + frow];  // the lane's token of subtile 0
+#pragma unroll
+                for (int mi = 0; mi < 8; ++mi) {
+                    if constexpr (ROLE == kCopyMid) {
+                        if (mi == kMidSubtile) issue(kb + 1, (int)((kb + 1) & 1));
+                    }
+                    const v8i af = afn;
+                    const float sa = san;
+                    if (mi < 7) {
+                        afn = frag(sta + (mi + 1) * 2048);
+                        san = sca[128 * wm + 16 * (mi + 1) + frow];
+                    }
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const v4f q = mfma_fp8(bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f});  // rows: weights
+                        fold(mi == 0 ? 7 : mi - 1, ni);
+                        pend[ni] = q;
+                    }
+                    ps = sa * sws;
+                }
             }
         }
-    }
+    };
+    if (wave < 2) kloop(std::integral_constant<int, kCopyTop>{});
+    else if (copier) kloop(std::integral_constant<int, kCopyMid>{});
+    else kloop(std::integral_constant<int, kComputeOnly>{});
     if constexpr (!MX) {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) fold(7, ni);
