@@ -24,6 +24,8 @@
 // registers for the whole K loop.  Tiles are walked in bands of four M-tiles
 // (the N-tiles of a band share its activation rows) and consecutive tiles are
 // kept on one XCD.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -134,36 +136,49 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(DParams p) {
         return *reinterpret_cast<const v8bf*>(base + o);
     };
 
-    for (int64_t ks = 0; ks < nstage; ++ks) {
-        if (copier) wait_vmcnt<0>();   // this wave's copies of step ks have landed
-        __builtin_amdgcn_s_barrier();  // ... and every other wave's; step ks-1 is free
-        if (copier) issue(ks + 1, (int)((ks + 1) & 1));
-        const uint8_t* st = ring[ks & 1];
-        const uint8_t* sta = st + SA + 64 * wm * 128;
-        const uint8_t* stb = st + SB + 16 * NI * wn * 128;
-        v8bf blo[NI], bhi[NI];
+    // The K loop, instantiated per wave role so that no branch sits among the
+    // MFMAs: waves 0-1 copy their half of a step right after the barrier,
+    // waves 2-3 before subtile kMid's MFMAs, waves 4-7 only compute (two
+    // half-size bursts on the DMA path instead of one, as in the FP8 tile
+    // kernel; kMid measured best of 1, 2, 3).
+    constexpr int kCopyTop = 0, kCopyMid = 1, kComputeOnly = 2, kMid = 2;
+    auto kloop = [&](auto role) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role)::value;
+        for (int64_t ks = 0; ks < nstage; ++ks) {
+            if (ROLE != kComputeOnly) wait_vmcnt<0>();  // this wave's copies of step ks have landed
+            __builtin_amdgcn_s_barrier();  // ... and every other wave's; step ks-1 is free
+            if (ROLE == kCopyTop) issue(ks + 1, (int)((ks + 1) & 1));
+            const uint8_t* st = ring[ks & 1];
+            const uint8_t* sta = st + SA + 64 * wm * 128;
+            const uint8_t* stb = st + SB + 16 * NI * wn * 128;
+            v8bf blo[NI], bhi[NI];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            blo[ni] = ld(stb + ni * 2048, lo_off);
-            bhi[ni] = ld(stb + ni * 2048, hi_off);
-        }
-        // activation fragments of subtile mi+1 are read while subtile mi runs
-        v8bf alo = ld(sta, lo_off), ahi = ld(sta, hi_off);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const v8bf a0 = alo, a1 = ahi;
-            if (mi < 3) {
-                alo = ld(sta + (mi + 1) * 2048, lo_off);
-                ahi = ld(sta + (mi + 1) * 2048, hi_off);
+            for (int ni = 0; ni < NI; ++ni) {
+                blo[ni] = ld(stb + ni * 2048, lo_off);
+                bhi[ni] = ld(stb + ni * 2048, hi_off);
             }
+            // activation fragments of subtile mi+1 are read while subtile mi runs
+            v8bf alo = ld(sta, lo_off), ahi = ld(sta, hi_off);
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, blo[ni], acc[mi][ni], 0, 0, 0);
+            for (int mi = 0; mi < 4; ++mi) {
+                if (ROLE == kCopyMid && mi == kMid) issue(ks + 1, (int)((ks + 1) & 1));
+                const v8bf a0 = alo, a1 = ahi;
+                if (mi < 3) {
+                    alo = ld(sta + (mi + 1) * 2048, lo_off);
+                    ahi = ld(sta + (mi + 1) * 2048, hi_off);
+                }
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bhi[ni], acc[mi][ni], 0, 0, 0);
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, blo[ni], acc[mi][ni], 0, 0, 0);
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bhi[ni], acc[mi][ni], 0, 0, 0);
+            }
         }
-    }
+    };
+    if (wave < 2) kloop(std::integral_constant<int, kCopyTop>{});
+    else if (copier) kloop(std::integral_constant<int, kCopyMid>{});
+    else kloop(std::integral_constant<int, kComputeOnly>{});
     wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
 
     // epilogue: bf16 (nearest even) through LDS, so that y is written as whole
