@@ -161,7 +161,7 @@ constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
 constexpr int TEROW = TBN + 8;      // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
 constexpr int kTilePrefetch = 2;    // L2 prefetch distance in K-blocks (measured best of 2, 3, 4, 6)
 constexpr int kCopyTop = 0, kCopyMid = 1, kComputeOnly = 2;  // wave roles in the K loop
-constexpr int kMidSubtile = 4;  // waves 2-3 copy before this subtile's MFMAs (measured best of 2, 3, 4, 6)
+constexpr int kMidSubtile = 4;  // waves 2-3 copy before this subtile's MFMAs (2, 3, 4 measured alike; 6 slower)
 static_assert(TBM * TEROW * 2 <= TNS * TSTAGE, "the epilogue tile fits in the ring");
 
 template <bool MX, bool W1>
@@ -407,7 +407,8 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
 
     // epilogue: bf16 (nearest even) through LDS, so that z[t][g][n] is written
     // as whole 512-byte tile rows with 16-byte stores (a lane's results are
-    // one column of 4 rows, which would be 2-byte scattered stores)
+    // four rows of one column, or four columns of one row: 2- or 8-byte
+    // scattered stores if written directly)
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring
     uint16_t* stile = reinterpret_cast<uint16_t*>(&ring[0][0]);  // [256][TEROW] bf16
 #pragma unroll
