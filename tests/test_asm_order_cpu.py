@@ -11,6 +11,9 @@ the barrier opens.  That is sound only if, in the generated code:
   wave's stores have) stand between the last such store and the arrival.
 The test compiles gemm_fp8.hip with the library's own flags and checks this
 in all eight instantiations of the kernel.
+
+The same listings (and gemm_bf16.hip's) also show that no GEMM kernel spills
+registers to scratch memory.
 """
 import os
 import re
@@ -66,3 +69,38 @@ def test_plain_gemm_kernels_have_no_atomics(asm):
         assert len(fns) == 4, pattern
         for name, lines in fns:
             assert not any("atomic" in ln for ln in lines), name
+
+
+def _resources(text: str):
+    """(kernel symbol, VGPRs, private segment bytes) for every kernel in an
+    assembly listing."""
+    for m in re.finditer(r"^\s*\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.M | re.S):
+        body = m.group(2)
+        vgpr = int(re.search(r"\.amdhsa_next_free_vgpr (\d+)", body).group(1))
+        scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1))
+        yield m.group(1), vgpr, scratch
+
+
+def test_gemm_kernels_do_not_spill(asm):
+    # every GEMM kernel keeps its accumulators, fragments and copy offsets in
+    # registers: a spill to scratch memory inside the K loop costs more than
+    # any schedule change gains (two waves per SIMD leave 256 VGPRs each)
+    found = list(_resources(asm))
+    assert len(found) >= 16, [k for k, _, _ in found]
+    for name, vgpr, scratch in found:
+        assert scratch == 0, (name, scratch)
+        assert vgpr <= 256, (name, vgpr)
+
+
+def test_bf16_gemm_kernels_do_not_spill(tmp_path):
+    from attention_output_projection_amd import build as b
+
+    if not os.path.exists(b.HIPCC):
+        pytest.skip(f"{b.HIPCC} not available")
+    out = tmp_path / "gemm_bf16.s"
+    cmd = [b.HIPCC, *b.FLAGS, "--cuda-device-only", "-S", os.path.join(b.CSRC, "gemm_bf16.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=900)
+    found = list(_resources(out.read_text()))
+    assert len(found) >= 4, [k for k, _, _ in found]
+    for name, vgpr, scratch in found:
+        assert scratch == 0, (name, scratch)
