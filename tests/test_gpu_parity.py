@@ -348,6 +348,32 @@ def test_grouped_gemm_ragged(T, G, R, brows, pow2):
     assert e <= TOL, e
 
 
+def _random_tile_shapes(n: int, seed: int):
+    """Seeded random shapes on the tile kernel (T > 128): ragged M- and N-tiles,
+    K-block counts 4 to 16, both weight-block layouts and both scale recipes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.integers(129, 601)), int(rng.integers(1, 4)), 64 * int(rng.integers(1, 6)),
+                    int(rng.choice([1, 2, 4])), int(rng.choice([1, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("T,G,R,hpg,brows,pow2", _random_tile_shapes(12, 2024))
+def test_grouped_gemm_random_tile_shapes(T, G, R, hpg, brows, pow2):
+    """Every output of the tile kernel (all three wave roles of its K loop,
+    the weights-as-rows promotion, the MX path) against the oracle."""
+    w = wl.Workload(300 + T + G + R, "rnd", T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=R,
+                    max_pos=4096, positions="uniform", pow2=pow2, w_block_rows=brows)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, hpg, pow2=pow2)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    ref = oracle.grouped_gemm(qr, sr, qwr, swr, G, R, brows)
+    zg = gpu_gemm(w, qr, sr, d_wq, d_ws, brows, pow2)
+    e = U.rel_max_err(zg, ref)
+    assert e <= TOL, e
+
+
 def test_grouped_gemm_group_isolation_on_gpu():
     """Changing weight rows of other groups leaves a group's output unchanged."""
     w = wl.Workload(80, "iso", T=40, n_groups=3, heads_per_group=8, o_lora_rank=128, max_pos=4096,
