@@ -13,11 +13,13 @@
 // 512-thread workgroup, eight waves as 4 (M) x 2 (N) of 64 x (16*NI), one
 // 64-deep K-step (128 bytes of every row) per stage, stages double-buffered in
 // LDS and filled by DMA copies (global_load_lds) into XOR-swizzled 128-byte
-// rows.  Waves 0-3 issue the copies, waves 4-7 only compute.  NI = 8 gives
-// 256x256 tiles; NI = 7 gives 256x224 tiles, which the launcher picks when
-// they divide the grid into fuller rounds of 256 workgroups (hidden = 7168 =
-// 32 x 224); NI = 2 gives 256x64 tiles for grids too small to fill the
-// chip with wide tiles (few tokens).  MFMA v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a
+// rows.  Waves 0-3 issue the copies (waves 0-1 right after the barrier,
+// waves 2-3 in the middle of the K-step: two half-size bursts on the DMA
+// path), waves 4-7 only compute.  NI = 8 gives 256x256 tiles; NI = 7 gives
+// 256x224 tiles, which the launcher picks when they divide the grid into
+// fuller rounds of 256 workgroups (hidden = 7168 = 32 x 224); NI = 2 gives
+// 256x64 tiles for grids too small to fill the chip with wide tiles (few
+// tokens).  MFMA v_mfma_f32_16x16x32_bf16: a lane's two 16-byte pieces of a
 // row (pieces 2q and 2q+1 for lane group q) feed the two K=32 halves of the
 // step, in the same order for both operands, so the pair of MFMAs sums the
 // whole 64-deep step.  The accumulators stay in the matrix-core result
