@@ -25,20 +25,25 @@
 //    v_mfma_scale_f32_16x16x128_f8f6f4 applies the E8M0 exponents of sa and
 //    sw in the matrix core and accumulates directly; no VALU work per block.
 //
-// Two kernels share this machinery, both fed by direct global->LDS copies
+// The kernels share this machinery, all fed by direct global->LDS copies
 // (global_load_lds) into rings of 128-byte rows whose 16-byte pieces are
 // XOR-swizzled so fragment reads hit distinct banks:
-//  * tile kernel (large T): 256x256 output tile per 512-thread workgroup,
-//    eight waves of 128x64, one K-block per stage, double-buffered;
+//  * tile kernels (large T): 256x256 output tile per 512-thread workgroup,
+//    eight waves of 128x64, one K-block per stage, double-buffered.  The
+//    persistent form (one workgroup per CU walking its tiles, the next
+//    tile's first stage copied during the last K-block) serves the fp32
+//    recipe with 128x128 weight blocks and the pow2 recipe; the fp32 recipe
+//    with per-row weight scales keeps one tile per workgroup (its persistent
+//    form does not fit the register file);
 //  * decode kernel (small T): 64x64 output tile per workgroup, two K-groups
 //    of four waves (16 columns each) with a four-stage ring each, the two
 //    partial tiles summed through LDS at the end.  The weight stream is the
 //    cost at small T; the deep ring keeps enough of it in flight.
-// Both remap workgroups so that tiles of one group land on one XCD (a group's
-// activations and weights then stay in that XCD's L2).  A third kernel runs
-// the decode kernel's grid with the quantisation (steps a1 + a2) in front:
-// each workgroup quantises its share of its group into a workspace, the
-// group's workgroups meet at a barrier of their own, then each runs its tile.
+// All of them take the tiles of one group on one XCD (a group's activations
+// and weights then stay in that XCD's L2).  A further kernel runs the decode
+// kernel's grid with the quantisation (steps a1 + a2) in front: each
+// workgroup quantises its share of its group into a workspace, the group's
+// workgroups meet at a barrier of their own, then each runs its tile.
 #include <cstdlib>
 #include <type_traits>
 
@@ -77,6 +82,8 @@ struct GParams {
     uint32_t xcd_per = 0;  // tiles per XCD when the XCD remap applies, else 0
     int xcd_shift = 0;     // log2 of the XCD count (a power of two) when it applies
     int pfd = 0;   // tile kernels: L2 prefetch distance in K-blocks (0: none)
+    uint32_t ntot = 0;  // persistent tile kernel: tiles in all
+    int xnext = 0;      // persistent tile kernel: every N-tile is whole (R a multiple of 256)
 };
 
 // Exponent byte (E8M0) of activation scale word `raw` for K-block kb: the
@@ -441,6 +448,368 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
         const uint4 v = *reinterpret_cast<const uint4*>(stile + r * TEROW + 8 * l32);
         if (row < p.T && col < p.R) *reinterpret_cast<uint4*>(p.z + (row * p.G + g) * p.R + col) = v;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent tile kernel: the tile kernel's K loop, with one workgroup per CU
+// walking a sequence of tiles.  The tiles of an XCD are taken in the same
+// order as the one-tile-per-workgroup grid (at any time an XCD's workgroups
+// run consecutive tile ids: the N-tiles of 8 M-tiles of one group), and:
+//  * the last K-block of a tile copies the next tile's first stage into the
+//    free ring slot (in place of a re-copy of the last block), so that stage
+//    lands while the tile's results are written;
+//  * each wave writes its own 128x64 results, one 16-row subtile at a time,
+//    through a private 16-row LDS buffer as whole 128-byte z row segments:
+//    no workgroup barrier between the K loop and the stores, and the ring
+//    stays free for the next tile's copies.
+// The copy offsets are lane constants plus per-tile scalar bases; a tile cut
+// short by T or R clamps its rows, so its first stage is copied by itself
+// (after the previous tile's re-copy has landed).
+constexpr int PEROW = 64 + 8;  // bf16 per row of a wave's epilogue subtile (16-byte pad)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> two bf16 (round to nearest even) in one word, low half first.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Tiles of this workgroup: base + first + i * step while first + i * step < limit.
+struct TileSeq {
+    uint32_t base, first, step, limit;
+};
+__device__ __forceinline__ TileSeq tile_seq(const GParams& p) {
+    const uint32_t b = blockIdx.x, n = gridDim.x;
+    if (p.xcd_per) {
+        const uint32_t x = b & ((1u << p.xcd_shift) - 1u);
+        return {x * p.xcd_per, b >> p.xcd_shift, n >> p.xcd_shift, p.xcd_per};
+    }
+    return {0u, b, n, p.ntot};
+}
+
+// Scalar description of one tile: operand bases at K-block 0 and the last
+// valid tile-local row (mlim) and weight row (nlim).
+struct TilePlan {
+    const uint8_t* ab;   // activation row m0 of group g
+    const uint8_t* wb;   // weight row g*R + n0
+    const uint8_t* sab;  // activation scale word of row m0
+    const uint8_t* swb;  // weight scale word of the block holding row g*R + n0
+    int32_t mlim, nlim;
+    int32_t wphase;      // (g*R + n0) mod the weight scale block height
+    int32_t mt, nt;
+    int64_t g, m0, n0;
+    bool full;
+};
+template <typename PP>
+__device__ __forceinline__ TilePlan tile_plan(const PP& p, uint32_t t) {
+    const uint32_t g = t / p.tpg, r = t - g * p.tpg, mt = r / p.nt32, nt = r - mt * p.nt32;
+    TilePlan q;
+    q.g = g;
+    q.mt = (int32_t)mt;
+    q.nt = (int32_t)nt;
+    q.m0 = (int64_t)mt * TBM;
+    q.n0 = (int64_t)nt * TBN;
+    const int64_t ml = p.T - 1 - q.m0, nl = p.R - 1 - q.n0;
+    q.mlim = (int32_t)(ml < TBM ? ml : TBM);
+    q.nlim = (int32_t)(nl < TBN ? nl : TBN);
+    const int64_t wrow = (int64_t)g * p.R + q.n0;
+    q.wphase = (int32_t)(wrow & ((1 << p.w_shift) - 1));
+    q.ab = p.a + (int64_t)g * p.sg + q.m0 * p.st;
+    q.wb = p.w + wrow * p.D;
+    q.sab = reinterpret_cast<const uint8_t*>(p.sa + (int64_t)g * p.ssg + q.m0 * p.sst);
+    q.swb = reinterpret_cast<const uint8_t*>(p.sw + (wrow >> p.w_shift) * p.kbw);
+    q.full = q.mlim >= TBM - 1 && q.nlim >= TBN - 1;
+    return q;
+}
+
+// The kernel's parameters re-read from the kernel-argument segment through a
+// pointer the compiler cannot see through: values a tile transition needs are
+// then loaded again at each transition instead of being held in scalar
+// registers across the K loop (which has none to spare).  GParams is the
+// kernel's only argument, at offset 0 of the segment.
+typedef __attribute__((address_space(4))) const GParams KGParams;
+__device__ __forceinline__ KGParams& params_reloaded() {
+    uint64_t v = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(v));
+    return *reinterpret_cast<KGParams*>(v);
+}
+
+template <bool MX, bool W1>
+__global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[TNS][TSTAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t epi[TNW][16 * PEROW];
+    __shared__ __attribute__((aligned(256))) uint8_t pf_sink[256];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+    const int wm = wave & 1, wn = wave >> 1;
+    const bool copier = wave < 4;  // wave-uniform
+    const TileSeq seq = tile_seq(p);
+
+    // ---- copy plan of copying wave c (0-3): activation rows 64c..64c+63 and
+    // weight rows 64c..64c+63 of the tile (8 rows of 128 bytes per
+    // instruction) and the scales of those rows; lane offsets relative to the
+    // tile's scalar bases, rows clamped to the tile's last valid row.
+    uint32_t off[16], soffa = 0, soffw = 0;
+    auto plan_lanes = [&](KGParams& pr, const TilePlan& q) __attribute__((always_inline)) {
+        if (copier) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 64 * wave + 8 * j + (lane >> 3);
+                const uint32_t piece = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+                off[j] = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.st + piece;
+                off[8 + j] = (uint32_t)(row < q.nlim ? row : q.nlim) * (uint32_t)pr.D + piece;
+            }
+            const int row = 64 * wave + lane;
+            soffa = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.sst * 4u;
+            soffw = (uint32_t)(((q.wphase + (row < q.nlim ? row : q.nlim)) >> pr.w_shift) * pr.kbw) * 4u;
+        }
+    };
+    const uint32_t ring0 = lds_offset(&ring[0][0]);
+    const uint32_t adst = ring0 + TSA + 64 * (wave & 3) * 128, wdst = ring0 + TSB + 64 * (wave & 3) * 128;
+    auto issue = [&](const uint8_t* ab, const uint8_t* wb, const uint8_t* sab, const uint8_t* swb, int64_t kb,
+                     int slot) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)(slot * TSTAGE);
+        ab += kb * 128;
+        wb += kb * 128;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16s(ab, off[j], adst + so + j * 1024);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16s(wb, off[8 + j], wdst + so + j * 1024);
+        dma4s(sab + (kb >> p.kshift) * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
+        dma4s(swb + (kb >> p.wkshift) * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
+    };
+
+    // L2 prefetch shared out among an XCD's co-running tiles, as in the tile
+    // kernel: N-tile nt < 4 touches activation rows 64*nt..64*nt+63 of its
+    // M-tile's slab (wave 0), M-tile mt touches weight rows 32*(mt%8)..+31 of
+    // its N-tile's slab (wave 1), pfd K-blocks ahead of the copies.
+    uint32_t pfoff = 0;
+    const uint32_t sink = lds_offset(pf_sink);
+    auto plan_pf = [&](KGParams& pr, const TilePlan& q) __attribute__((always_inline)) {
+        if (wave == 0) {
+            const int row = 64 * q.nt + lane;
+            pfoff = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.st;
+        } else if (wave == 1) {
+            const int row = 32 * (q.mt & 7) + (lane & 31);
+            pfoff = (uint32_t)(row < q.nlim ? row : q.nlim) * (uint32_t)pr.D;
+        }
+    };
+
+    v4f acc[8][4];
+    const int frow = lane & 15;
+    const int p0 = 2 * (lane >> 4);
+    const int lo_off = frow * 128 + 16 * (p0 ^ swz(frow));
+    const int hi_off = frow * 128 + 16 * ((p0 + 1) ^ swz(frow));
+    auto frag = [&](const uint8_t* base) __attribute__((always_inline)) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + lo_off);
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + hi_off);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    v4f pend[4];
+    float ps = 0.f;
+    float psa[4] = {0.f, 0.f, 0.f, 0.f}, psw[4] = {0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](int mi, int ni) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[mi][ni][i] = __builtin_fmaf(pend[ni][i], W1 ? psa[i] * psw[ni] : ps, acc[mi][ni][i]);
+    };
+
+    // Subtile mi (16 token rows x 64 columns) of this wave's results to z:
+    // bf16 (nearest even) into the wave's buffer, then 8 rows of 128 bytes per
+    // store.  zb points at z[m0 + 128*wm][g][n0 + 64*wn]; rows_left and
+    // cols_left bound the tile by T and R.
+    auto store_sub = [&](int mi, uint16_t* zb, int64_t zrs, int64_t rows_left, int64_t cols_left)
+                         __attribute__((always_inline)) {
+        int el = lane;  // lane-derived addresses computed here, not held across the K loop
+        asm volatile("" : "+v"(el));
+        const int efrow = el & 15;
+        uint16_t* my = &epi[wave][0];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const uint32_t v01 = pk_bf16(acc[mi][ni][0], acc[mi][ni][1]);
+            const uint32_t v23 = pk_bf16(acc[mi][ni][2], acc[mi][ni][3]);
+            if constexpr (MX || W1) {  // a lane holds one column of four rows
+                uint16_t* col = my + 4 * (el >> 4) * PEROW + 16 * ni + efrow;
+                col[0] = (uint16_t)v01;
+                col[PEROW] = (uint16_t)(v01 >> 16);
+                col[2 * PEROW] = (uint16_t)v23;
+                col[3 * PEROW] = (uint16_t)(v23 >> 16);
+            } else {  // a lane holds four adjacent columns of one row
+                *reinterpret_cast<uint2*>(my + efrow * PEROW + 16 * ni + 4 * (el >> 4)) = uint2{v01, v23};
+            }
+        }
+        const int c8 = 8 * (el & 7);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 8 * h + (el >> 3);
+            const uint4 v = *reinterpret_cast<const uint4*>(my + r * PEROW + c8);
+            const int row = 16 * mi + r;
+            if (row < rows_left && c8 < cols_left) *reinterpret_cast<uint4*>(zb + row * zrs + c8) = v;
+        }
+    };
+
+    // The tile loop and its K loop, instantiated per wave role as in the tile
+    // kernel (waves 0-1 copy after the barrier, waves 2-3 before subtile
+    // kMidSubtile, waves 4-7 only compute).
+    auto run = [&](auto role) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role)::value;
+        constexpr bool COPY = ROLE != kComputeOnly;
+        bool first = true, chained = false;
+        for (uint32_t i = seq.first; i < seq.limit; i += seq.step) {
+            const TilePlan q = tile_plan(params_reloaded(), seq.base + i);
+            if constexpr (COPY) {
+                plan_lanes(params_reloaded(), q);
+                if (!chained) {
+                    if (!first) wait_vmcnt<0>();  // the re-copy into slot 0 has landed
+                    issue(q.ab, q.wb, q.sab, q.swb, 0, 0);
+                }
+            }
+            if constexpr (ROLE == kCopyTop) plan_pf(params_reloaded(), q);
+            first = false;
+            const uint32_t inext = i + seq.step;
+            const bool has_next = inext < seq.limit;
+            // the next tile's first stage rides on this tile's last copies
+            // when both tiles use the same lane offsets
+            const uint8_t *nab = q.ab, *nwb = q.wb, *nsab = q.sab, *nswb = q.swb;
+            bool chain = false;
+            if (has_next && p.xnext && q.full) {
+                const TilePlan qn = tile_plan(params_reloaded(), seq.base + inext);
+                chain = qn.full;
+                nab = qn.ab;
+                nwb = qn.wb;
+                nsab = qn.sab;
+                nswb = qn.swb;
+            }
+            chained = chain;
+            const bool pf = p.pfd > 0 && ROLE == kCopyTop && (wave == 1 || q.nt < 4);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) pend[ni] = v4f{0.f, 0.f, 0.f, 0.f};
+            auto issue_next = [&](int64_t kb) __attribute__((always_inline)) {
+                // stage kb + 1 of this tile, or the next tile's stage 0, or
+                // (neither) a re-copy of the last block into the free slot
+                const bool last = kb + 1 >= p.KB;
+                const bool nx = last && chain;
+                const int64_t k = last ? (nx ? 0 : p.KB - 1) : kb + 1;
+                issue(nx ? nab : q.ab, nx ? nwb : q.wb, nx ? nsab : q.sab, nx ? nswb : q.swb, k, (int)((kb + 1) & 1));
+            };
+            auto kblock = [&](int64_t kb) __attribute__((always_inline)) {
+                if constexpr (ROLE == kCopyTop) {
+                    if (pf && kb > 0 && kb + p.pfd < p.KB) wait_vmcnt<1>();
+                    else wait_vmcnt<0>();
+                } else if constexpr (ROLE == kCopyMid) {
+                    wait_vmcnt<0>();
+                }
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kb-1 are done
+                __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
+                if constexpr (ROLE == kCopyTop) {
+                    issue_next(kb);
+                    if (pf && kb + 1 + p.pfd < p.KB)
+                        dma4s((wave == 0 ? q.ab : q.wb) + (kb + 1 + p.pfd) * 128, pfoff, sink);
+                }
+                const uint8_t* st = ring[kb & 1];
+                const uint8_t* sta = st + TSA + 128 * wm * 128;
+                const uint8_t* stb = st + TSB + 64 * wn * 128;
+                const float* sca = reinterpret_cast<const float*>(st + TSS);
+                const float* scw = reinterpret_cast<const float*>(st + TSW);
+                v8i bfr[4];
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) bfr[ni] = frag(stb + ni * 2048);
+                v8i afn = frag(sta);
+                if constexpr (MX) {
+                    int eb[4];
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        eb[ni] = w_e8m0(p, __float_as_uint(scw[64 * wn + 16 * ni + frow]), kb);
+                    float san = sca[128 * wm + frow];
+#pragma unroll
+                    for (int mi = 0; mi < 8; ++mi) {
+                        if constexpr (ROLE == kCopyMid) {
+                            if (mi == kMidSubtile) issue_next(kb);
+                        }
+                        const v8i af = afn;
+                        const int ea = act_e8m0(p, __float_as_uint(san), kb);
+                        if (mi < 7) {
+                            afn = frag(sta + (mi + 1) * 2048);
+                            san = sca[128 * wm + 16 * (mi + 1) + frow];
+                        }
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
+                    }
+                } else if constexpr (W1) {
+                    float swv[4];
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
+                    const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * (128 * wm + 4 * (lane >> 4));
+                    float4 tn = *reinterpret_cast<const float4*>(sab);
+#pragma unroll
+                    for (int mi = 0; mi < 8; ++mi) {
+                        if constexpr (ROLE == kCopyMid) {
+                            if (mi == kMidSubtile) issue_next(kb);
+                        }
+                        const v8i af = afn;
+                        const float sa4[4] = {tn.x, tn.y, tn.z, tn.w};
+                        if (mi < 7) {
+                            afn = frag(sta + (mi + 1) * 2048);
+                            tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
+                        }
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const v4f qv = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
+                            fold(mi == 0 ? 7 : mi - 1, ni);
+                            pend[ni] = qv;
+                            if (mi == 0) psw[ni] = swv[ni];
+                        }
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) psa[k] = sa4[k];
+                    }
+                } else {
+                    const float sws = scw[64 * wn];
+                    float san = sca[128 * wm + frow];
+#pragma unroll
+                    for (int mi = 0; mi < 8; ++mi) {
+                        if constexpr (ROLE == kCopyMid) {
+                            if (mi == kMidSubtile) issue_next(kb);
+                        }
+                        const v8i af = afn;
+                        const float sa = san;
+                        if (mi < 7) {
+                            afn = frag(sta + (mi + 1) * 2048);
+                            san = sca[128 * wm + 16 * (mi + 1) + frow];
+                        }
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) {
+                            const v4f qv = mfma_fp8(bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f});
+                            fold(mi == 0 ? 7 : mi - 1, ni);
+                            pend[ni] = qv;
+                        }
+                        ps = sa * sws;
+                    }
+                }
+            };
+#pragma clang loop unroll(disable)
+            for (int64_t kb = 0; kb < p.KB; ++kb) kblock(kb);
+            if constexpr (!MX) {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) fold(7, ni);
+            }
+            // this wave's results to z, subtile by subtile
+            KGParams& pr = params_reloaded();
+            const int64_t r0 = q.m0 + 128 * wm, c0 = q.n0 + 64 * wn, zrs = pr.G * pr.R;
+            uint16_t* zb = pr.z + r0 * zrs + q.g * pr.R + c0;
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) store_sub(mi, zb, zrs, pr.T - r0, pr.R - c0);
+        }
+    };
+    if (wave < 2) run(std::integral_constant<int, kCopyTop>{});
+    else if (copier) run(std::integral_constant<int, kCopyMid>{});
+    else run(std::integral_constant<int, kComputeOnly>{});
+    wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
 }
 
 // ---------------------------------------------------------------------------
@@ -918,18 +1287,34 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
         p.mtiles = (a.T + TBM - 1) / TBM;
         p.ntiles = (a.R + TBN - 1) / TBN;
         if (!set_tile_map(p, TNW * 64)) return hipErrorInvalidConfiguration;
-        const dim3 grid(p.tpg * (uint32_t)p.G);
         p.pfd = kTilePrefetch;
+        if (!a.mx && a.w_1x128) {
+            // fp32 scales with per-row weight scales: one tile per workgroup (the
+            // persistent form of this instantiation does not fit the register file)
+            hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, true>), dim3(p.tpg * (uint32_t)p.G), dim3(TNW * 64), 0,
+                               stream, p);
+            return hipGetLastError();
+        }
+        // persistent grid: at most one workgroup per CU, the same number on every XCD
+        const uint32_t nblocks = p.tpg * (uint32_t)p.G;
+        const DeviceInfo dev = current_device_info();
+        uint32_t wgs;
+        if (p.xcd_per) {
+            const uint32_t per = (uint32_t)(dev.cus >> p.xcd_shift);
+            wgs = (per < p.xcd_per ? (per > 0 ? per : 1u) : p.xcd_per) << p.xcd_shift;
+        } else {
+            wgs = nblocks < (uint32_t)dev.cus ? nblocks : (uint32_t)dev.cus;
+        }
+        p.ntot = nblocks;
+        p.xnext = a.R % TBN == 0;
+        const dim3 grid(wgs);
         if (a.mx) {
             if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, true>), grid, dim3(TNW * 64), 0, stream, p);
+                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<true, true>), grid, dim3(TNW * 64), 0, stream, p);
             else
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<true, false>), grid, dim3(TNW * 64), 0, stream, p);
+                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<true, false>), grid, dim3(TNW * 64), 0, stream, p);
         } else {
-            if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, true>), grid, dim3(TNW * 64), 0, stream, p);
-            else
-                hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, false>), grid, dim3(TNW * 64), 0, stream, p);
+            hipLaunchKernelGGL((gemm_fp8_ptile_kernel<false, false>), grid, dim3(TNW * 64), 0, stream, p);
         }
     }
     return hipGetLastError();
