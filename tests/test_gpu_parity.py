@@ -374,6 +374,29 @@ def test_grouped_gemm_random_tile_shapes(T, G, R, hpg, brows, pow2):
     assert e <= TOL, e
 
 
+# Tile walks of the persistent tile kernel (one workgroup per CU, several
+# tiles each): 276 tiles (not a multiple of the XCD count: plain order), 320
+# and 544 tiles (XCD order), a ragged last M-tile (the next tile's first
+# stage is then copied by that tile itself), R = 320 (ragged N-tiles, no
+# chaining at all), both recipes and both weight-block layouts (fp32 with
+# per-row weight scales runs the one-tile-per-workgroup kernel).
+@pytest.mark.parametrize("T,G,hpg,R,brows,pow2", [(5639, 3, 2, 1024, 128, False), (2404, 8, 2, 1024, 128, False),
+                                                  (4100, 16, 2, 320, 128, False), (2404, 8, 2, 1024, 128, True),
+                                                  (2404, 8, 2, 1024, 1, True), (2404, 8, 2, 1024, 1, False)])
+def test_grouped_gemm_persistent_tile_walks(T, G, hpg, R, brows, pow2):
+    """Every output against the oracle's whole-tensor GEMM."""
+    w = wl.Workload(400 + T + G + R + brows, "walk", T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=R,
+                    max_pos=4096, positions="uniform", pow2=pow2, w_block_rows=brows)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, hpg, pow2=pow2)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    U.assert_scales_bitexact(_host(d_ws), swr)
+    ref = oracle.grouped_gemm_full(qr, sr, qwr, swr, G, R, brows)
+    zg = gpu_gemm(w, qr, sr, d_wq, d_ws, brows, pow2)
+    e = U.rel_max_err(zg, ref)
+    assert e <= TOL, e
+
+
 def test_grouped_gemm_group_isolation_on_gpu():
     """Changing weight rows of other groups leaves a group's output unchanged."""
     w = wl.Workload(80, "iso", T=40, n_groups=3, heads_per_group=8, o_lora_rank=128, max_pos=4096,
