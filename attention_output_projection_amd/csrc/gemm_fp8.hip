@@ -28,13 +28,10 @@
 // The kernels share this machinery, all fed by direct global->LDS copies
 // (global_load_lds) into rings of 128-byte rows whose 16-byte pieces are
 // XOR-swizzled so fragment reads hit distinct banks:
-//  * tile kernels (large T): 256x256 output tile per 512-thread workgroup,
-//    eight waves of 128x64, one K-block per stage, double-buffered.  The
-//    persistent form (one workgroup per CU walking its tiles, the next
-//    tile's first stage copied during the last K-block) serves the fp32
-//    recipe with 128x128 weight blocks and the pow2 recipe; the fp32 recipe
-//    with per-row weight scales keeps one tile per workgroup (its persistent
-//    form does not fit the register file);
+//  * tile kernel (large T): 256x256 output tiles, 512-thread workgroups of
+//    eight waves of 128x64, one K-block per stage, double-buffered; one
+//    workgroup per CU walks its tiles, the next tile's first stage copied
+//    during the last K-block;
 //  * decode kernel (small T): 64x64 output tile per workgroup, two K-groups
 //    of four waves (16 columns each) with a four-stage ring each, the two
 //    partial tiles summed through LDS at the end.  The weight stream is the
@@ -130,9 +127,10 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel (large T): 256x256 output tile per 512-thread workgroup, eight
-// waves as 2 (M) x 4 (N) of 128x64 (32 MFMAs per K-block per wave, 128 fp32
-// accumulators in VGPRs), two waves per SIMD.  The tile and wave shapes keep
+// Tile kernel (large T): 256x256 output tiles, one 512-thread workgroup per
+// CU walking a sequence of tiles (below), eight waves as 2 (M) x 4 (N) of
+// 128x64 (32 MFMAs per K-block per wave, 128 fp32 accumulators in VGPRs),
+// two waves per SIMD.  The tile and wave shapes keep
 // LDS reads per MFMA low: per K-block the workgroup reads 192 KiB of
 // fragments and copies 64 KiB for 2048 MFMA cycles per SIMD.  Each K-block is
 // one pipeline stage (256x128-byte activation slab, 256x128-byte weight slab,
@@ -165,296 +163,14 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 constexpr int TBM = 256, TBN = 256, TNS = 2, TNW = 8;
 constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
 constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
-constexpr int TEROW = TBN + 8;      // bf16 per row of the epilogue tile (16-byte pad against bank conflicts)
 constexpr int kTilePrefetch = 2;    // L2 prefetch distance in K-blocks (measured best of 2, 3, 4, 6)
 constexpr int kCopyTop = 0, kCopyMid = 1, kComputeOnly = 2;  // wave roles in the K loop
 constexpr int kMidSubtile = 4;  // waves 2-3 copy before this subtile's MFMAs (2, 3, 4 measured alike; 6 slower)
-static_assert(TBM * TEROW * 2 <= TNS * TSTAGE, "the epilogue tile fits in the ring");
 
-template <bool MX, bool W1>
-__global__ __launch_bounds__(TNW * 64) void gemm_fp8_tile_kernel(GParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[TNS][TSTAGE];
-    __shared__ __attribute__((aligned(256))) uint8_t pf_sink[256];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
-    const int wm = wave & 1, wn = wave >> 1;
-    const TileCoord tc = tile_coord(p);
-    const int64_t g = tc.g, mt = tc.mt, nt = tc.nt;
-    const int64_t m0 = mt * TBM, n0 = nt * TBN;
-
-    // ---- copy plan.  Copying wave c (0-3) moves activation rows 64c..64c+63
-    // and weight rows 64c..64c+63 (8 rows of 128 bytes per instruction) and
-    // the scales of those rows and columns.  Sources are uniform bases
-    // (advanced per K-block) plus fixed 32-bit lane offsets (the host keeps
-    // every offset below 2^32).
-    const bool copier = wave < 4;  // wave-uniform
-    const uint8_t* abase = p.a + g * p.sg;
-    const uint8_t* wbase = p.w + g * p.R * p.D;
-    const uint8_t* sabase = reinterpret_cast<const uint8_t*>(p.sa + g * p.ssg);
-    const uint8_t* swbase = reinterpret_cast<const uint8_t*>(p.sw);
-    uint32_t off[16], soffa = 0, soffw = 0;
-    if (copier) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 64 * wave + 8 * j + (lane >> 3);
-            int64_t m = m0 + row;
-            m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
-            off[j] = (uint32_t)(m * p.st + ((lane & 7) ^ swz(row)) * 16);
-            int64_t n = n0 + row;
-            n = n < p.R ? n : p.R - 1;
-            off[8 + j] = (uint32_t)(n * p.D + ((lane & 7) ^ swz(row)) * 16);
-        }
-        int64_t m = m0 + 64 * wave + lane;
-        m = m < p.T ? m : p.T - 1;
-        soffa = (uint32_t)(m * p.sst * 4);
-        int64_t n = n0 + 64 * wave + lane;
-        n = n < p.R ? n : p.R - 1;
-        soffw = (uint32_t)(wscale_index(p, g * p.R + n, 0) * 4);
-    }
-    const uint32_t ring0 = lds_offset(&ring[0][0]);
-    const uint32_t adst = ring0 + TSA + 64 * (wave & 3) * 128, wdst = ring0 + TSB + 64 * (wave & 3) * 128;
-    auto issue = [&](int64_t kb, int slot) __attribute__((always_inline)) {
-        kb = kb < p.KB ? kb : p.KB - 1;  // past the end: re-copy the last block into a dead slot
-        const uint32_t so = (uint32_t)(slot * TSTAGE);
-        const uint8_t* ab = abase + kb * 128;
-        const uint8_t* wb = wbase + kb * 128;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16s(ab, off[j], adst + so + j * 1024);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16s(wb, off[8 + j], wdst + so + j * 1024);
-        dma4s(sabase + (kb >> p.kshift) * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
-        dma4s(swbase + (kb >> p.wkshift) * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
-    };
-
-    // L2 prefetch, shared out among the tiles that run together on one XCD
-    // (consecutive tile ids: the N-tiles of 8 M-tiles of one group): the
-    // N-tile nt < 4 of an M-tile touches activation rows 64*nt..64*nt+63 of
-    // the M-tile's slab, and M-tile mt touches weight rows 32*(mt%8) ..
-    // 32*(mt%8)+31 of the N-tile's slab, pfd K-blocks ahead of the copies,
-    // one 4-byte load per 128-byte line into a scratch LDS word.
-    const bool pfa = p.pfd > 0 && wave == 0 && nt < 4, pfw = p.pfd > 0 && wave == 1;
-    uint32_t pfoff = 0;
-    if (pfa) {
-        int64_t m = m0 + 64 * nt + lane;
-        m = m < p.T ? m : p.T - 1;
-        pfoff = (uint32_t)(m * p.st);
-    } else if (pfw) {
-        int64_t n = n0 + 32 * (mt & 7) + (lane & 31);
-        n = n < p.R ? n : p.R - 1;
-        pfoff = (uint32_t)(n * p.D);
-    }
-    const uint32_t sink = lds_offset(pf_sink);
-    auto prefetch = [&](int64_t kb) __attribute__((always_inline)) {
-        kb += p.pfd;
-        if (kb < p.KB) dma4s((pfa ? abase : wbase) + kb * 128, pfoff, sink);
-    };
-    const bool pf = pfa || pfw;  // wave-uniform
-
-    if (copier) issue(0, 0);
-
-    v4f acc[8][4];
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // fragment addressing: rows 16k + frow share the swizzle of frow, so a
-    // lane's two piece offsets are fixed and subtiles step by 2 KiB
-    const int frow = lane & 15;
-    const int p0 = 2 * (lane >> 4);
-    const int lo_off = frow * 128 + 16 * (p0 ^ swz(frow));
-    const int hi_off = frow * 128 + 16 * ((p0 + 1) ^ swz(frow));
-    auto frag = [&](const uint8_t* base) __attribute__((always_inline)) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + lo_off);
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + hi_off);
-        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    };
-
-    // fp32 recipe: the partials of the subtile issued last and their scale
-    // factors, folded into the accumulators one subtile later (the last
-    // subtile of a K-block across the barrier into the next K-block), so that
-    // the matrix core has the next subtile's MFMAs to run while they wait.
-    // With 128x128 weight blocks the weights are the MFMA's 16-row operand
-    // and the tokens its 16 columns: a lane's four partials are then four
-    // weight rows of one token and share one factor sa[token] * sw[block],
-    // one multiply per subtile instead of one per row.  With per-row weight
-    // scales the tokens stay the row operand (each partial has its own
-    // factor either way, and this form holds fewer of them).
-    v4f pend[4];
-    float ps = 0.f;                                                      // 128x128 blocks
-    float psa[4] = {0.f, 0.f, 0.f, 0.f}, psw[4] = {0.f, 0.f, 0.f, 0.f};  // per-row weight scales
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) pend[ni] = v4f{0.f, 0.f, 0.f, 0.f};
-    auto fold = [&](int mi, int ni) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[mi][ni][i] = __builtin_fmaf(pend[ni][i], W1 ? psa[i] * psw[ni] : ps, acc[mi][ni][i]);
-    };
-
-    // The K loop, instantiated per wave role so that no branch sits among the
-    // MFMAs: waves 0-1 copy their half of a stage right after the barrier
-    // (and issue the L2 prefetch), waves 2-3 after subtile kMidSubtile-1's
-    // MFMAs, waves 4-7 only compute.  Two half-size bursts on the DMA path
-    // hold each copying wave about half as long as one burst of all four.
-    // Not unrolled or peeled: a peeled first K-block is a second copy of the
-    // loop body, and that copy spills.
-    auto kloop = [&](auto role) __attribute__((always_inline)) {
-        constexpr int ROLE = decltype(role)::value;
-#pragma clang loop unroll(disable)
-        for (int64_t kb = 0; kb < p.KB; ++kb) {
-            // this wave's copies of stage kb have landed (a prefetch issued
-            // after them may still be in flight: loads complete in order)
-            if constexpr (ROLE == kCopyTop) {
-                if (pf && kb > 0 && kb + p.pfd < p.KB) wait_vmcnt<1>();
-                else wait_vmcnt<0>();
-            } else if constexpr (ROLE == kCopyMid) {
-                wait_vmcnt<0>();
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kb-1 are done
-            __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage kb-1 is free
-            if constexpr (ROLE == kCopyTop) {
-                issue(kb + 1, (int)((kb + 1) & 1));
-                if (pf) prefetch(kb + 1);
-            }
-            const uint8_t* st = ring[kb & 1];
-            const uint8_t* sta = st + TSA + 128 * wm * 128;
-            const uint8_t* stb = st + TSB + 64 * wn * 128;
-            const float* sca = reinterpret_cast<const float*>(st + TSS);
-            const float* scw = reinterpret_cast<const float*>(st + TSW);
-            v8i bfr[4];
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) bfr[ni] = frag(stb + ni * 2048);
-            // the activation fragment of subtile mi+1 (and its scales) is read
-            // from LDS while the MFMAs of subtile mi run; each subtile's four
-            // MFMAs are issued before their partials are folded into the
-            // accumulators
-            v8i afn = frag(sta);
-            if constexpr (MX) {
-                int eb[4];
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    eb[ni] = w_e8m0(p, __float_as_uint(scw[64 * wn + 16 * ni + frow]), kb);
-                float san = sca[128 * wm + frow];
-#pragma unroll
-                for (int mi = 0; mi < 8; ++mi) {
-                    if constexpr (ROLE == kCopyMid) {
-                        if (mi == kMidSubtile) issue(kb + 1, (int)((kb + 1) & 1));
-                    }
-                    const v8i af = afn;
-                    const int ea = act_e8m0(p, __float_as_uint(san), kb);
-                    if (mi < 7) {
-                        afn = frag(sta + (mi + 1) * 2048);
-                        san = sca[128 * wm + 16 * (mi + 1) + frow];
-                    }
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        acc[mi][ni] = mfma_fp8_mx(af, bfr[ni], acc[mi][ni], ea, eb[ni]);
-                }
-            } else if constexpr (W1) {
-                float swv[4];
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
-                const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * (128 * wm + 4 * (lane >> 4));
-                float4 tn = *reinterpret_cast<const float4*>(sab);  // the scales of the lane's four rows
-#pragma unroll
-                for (int mi = 0; mi < 8; ++mi) {
-                    if constexpr (ROLE == kCopyMid) {
-                        if (mi == kMidSubtile) issue(kb + 1, (int)((kb + 1) & 1));
-                    }
-                    const v8i af = afn;
-                    const float sa4[4] = {tn.x, tn.y, tn.z, tn.w};
-                    if (mi < 7) {
-                        afn = frag(sta + (mi + 1) * 2048);
-                        tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
-                    }
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4f q = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
-                        fold(mi == 0 ? 7 : mi - 1, ni);
-                        pend[ni] = q;
-                        if (mi == 0) psw[ni] = swv[ni];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) psa[i] = sa4[i];
-                }
-            } else {
-                const float sws = scw[64 * wn];  // one weight scale per 64-row span
-                float san = sca[128 * wm + frow];  // the lane's token of subtile 0
-#pragma unroll
-                for (int mi = 0; mi < 8; ++mi) {
-                    if constexpr (ROLE == kCopyMid) {
-                        if (mi == kMidSubtile) issue(kb + 1, (int)((kb + 1) & 1));
-                    }
-                    const v8i af = afn;
-                    const float sa = san;
-                    if (mi < 7) {
-                        afn = frag(sta + (mi + 1) * 2048);
-                        san = sca[128 * wm + 16 * (mi + 1) + frow];
-                    }
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const v4f q = mfma_fp8(bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f});  // rows: weights
-                        fold(mi == 0 ? 7 : mi - 1, ni);
-                        pend[ni] = q;
-                    }
-                    ps = sa * sws;
-                }
-            }
-        }
-    };
-    if (wave < 2) kloop(std::integral_constant<int, kCopyTop>{});
-    else if (copier) kloop(std::integral_constant<int, kCopyMid>{});
-    else kloop(std::integral_constant<int, kComputeOnly>{});
-    if constexpr (!MX) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) fold(7, ni);
-    }
-    wait_vmcnt<0>();  // no copy may still be writing LDS when the workgroup exits
-
-    // epilogue: bf16 (nearest even) through LDS, so that z[t][g][n] is written
-    // as whole 512-byte tile rows with 16-byte stores (a lane's results are
-    // four rows of one column, or four columns of one row: 2- or 8-byte
-    // scattered stores if written directly)
-    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
-    uint16_t* stile = reinterpret_cast<uint16_t*>(&ring[0][0]);  // [256][TEROW] bf16
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            if constexpr (MX || W1) {  // a lane holds one column of four rows
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 128 * wm + 16 * mi + 4 * (lane >> 4) + i;
-                    const int c = 64 * wn + 16 * ni + frow;
-                    stile[r * TEROW + c] = (uint16_t)f32_to_bf16_bits(acc[mi][ni][i]);
-                }
-            } else {  // a lane holds four adjacent columns of one row: one 8-byte write
-                const int r = 128 * wm + 16 * mi + frow;
-                const int c = 64 * wn + 16 * ni + 4 * (lane >> 4);
-                const uint2 v = {f32_to_bf16_bits(acc[mi][ni][0]) | (f32_to_bf16_bits(acc[mi][ni][1]) << 16),
-                                 f32_to_bf16_bits(acc[mi][ni][2]) | (f32_to_bf16_bits(acc[mi][ni][3]) << 16)};
-                *reinterpret_cast<uint2*>(stile + r * TEROW + c) = v;
-            }
-        }
-    __syncthreads();
-    // 32 lanes per row, 16 bytes each; a wave stores 2 rows per instruction
-    const int half = lane >> 5, l32 = lane & 31;
-    const int64_t col = n0 + 8 * l32;
-#pragma unroll 4
-    for (int k = 0; k < TBM / (2 * TNW); ++k) {
-        const int r = 2 * (TNW * k + wave) + half;
-        const int64_t row = m0 + r;
-        const uint4 v = *reinterpret_cast<const uint4*>(stile + r * TEROW + 8 * l32);
-        if (row < p.T && col < p.R) *reinterpret_cast<uint4*>(p.z + (row * p.G + g) * p.R + col) = v;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Persistent tile kernel: the tile kernel's K loop, with one workgroup per CU
-// walking a sequence of tiles.  The tiles of an XCD are taken in the same
-// order as the one-tile-per-workgroup grid (at any time an XCD's workgroups
-// run consecutive tile ids: the N-tiles of 8 M-tiles of one group), and:
+// Persistent grid: one workgroup per CU (the same number on every XCD) walks
+// a sequence of tiles.  The tiles of an XCD are taken in order of tile id
+// (at any time an XCD's workgroups run consecutive tile ids: the N-tiles of
+// 8 M-tiles of one group), and:
 //  * the last K-block of a tile copies the next tile's first stage into the
 //    free ring slot (in place of a re-copy of the last block), so that stage
 //    lands while the tile's results are written;
@@ -536,6 +252,7 @@ __device__ __forceinline__ KGParams& params_reloaded() {
 
 template <bool MX, bool W1>
 __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
+    constexpr bool kTight = W1 && !MX;  // the instantiation with the most live registers
     __shared__ __attribute__((aligned(1024))) uint8_t ring[TNS][TSTAGE];
     __shared__ __attribute__((aligned(16))) uint16_t epi[TNW][16 * PEROW];
     __shared__ __attribute__((aligned(256))) uint8_t pf_sink[256];
@@ -553,14 +270,19 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
     uint32_t off[16], soffa = 0, soffw = 0;
     auto plan_lanes = [&](KGParams& pr, const TilePlan& q) __attribute__((always_inline)) {
         if (copier) {
+            // fp32 with per-row weight scales (the instantiation with the most
+            // live registers): lane-derived values formed here, not held
+            // across the tile loop
+            int el = lane;
+            if constexpr (kTight) asm volatile("" : "+v"(el));
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int row = 64 * wave + 8 * j + (lane >> 3);
-                const uint32_t piece = (uint32_t)(((lane & 7) ^ swz(row)) * 16);
+                const int row = 64 * wave + 8 * j + (el >> 3);
+                const uint32_t piece = (uint32_t)(((el & 7) ^ swz(row)) * 16);
                 off[j] = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.st + piece;
                 off[8 + j] = (uint32_t)(row < q.nlim ? row : q.nlim) * (uint32_t)pr.D + piece;
             }
-            const int row = 64 * wave + lane;
+            const int row = 64 * wave + el;
             soffa = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.sst * 4u;
             soffw = (uint32_t)(((q.wphase + (row < q.nlim ? row : q.nlim)) >> pr.w_shift) * pr.kbw) * 4u;
         }
@@ -583,20 +305,41 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
     // L2 prefetch shared out among an XCD's co-running tiles, as in the tile
     // kernel: N-tile nt < 4 touches activation rows 64*nt..64*nt+63 of its
     // M-tile's slab (wave 0), M-tile mt touches weight rows 32*(mt%8)..+31 of
-    // its N-tile's slab (wave 1), pfd K-blocks ahead of the copies.
-    uint32_t pfoff = 0;
+    // its N-tile's slab (wave 1), pfd K-blocks ahead of the copies.  (The
+    // lane offset is formed at each touch from scalars: no register held
+    // across the K loop.)
     const uint32_t sink = lds_offset(pf_sink);
+    int32_t pf_row0 = 0, pf_lim = 0;
+    uint32_t pf_stride = 0, pfoff = 0;
+    auto pf_lane = [&](int el) __attribute__((always_inline)) {
+        const int row = pf_row0 + (wave == 0 ? el : (el & 31));
+        return (uint32_t)(row < pf_lim ? row : pf_lim) * pf_stride;
+    };
     auto plan_pf = [&](KGParams& pr, const TilePlan& q) __attribute__((always_inline)) {
         if (wave == 0) {
-            const int row = 64 * q.nt + lane;
-            pfoff = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.st;
+            pf_row0 = 64 * q.nt;
+            pf_lim = q.mlim;
+            pf_stride = (uint32_t)pr.st;
         } else if (wave == 1) {
-            const int row = 32 * (q.mt & 7) + (lane & 31);
-            pfoff = (uint32_t)(row < q.nlim ? row : q.nlim) * (uint32_t)pr.D;
+            pf_row0 = 32 * (q.mt & 7);
+            pf_lim = q.nlim;
+            pf_stride = (uint32_t)pr.D;
+        }
+        if constexpr (!kTight) pfoff = pf_lane(lane);
+    };
+    auto pf_off = [&]() __attribute__((always_inline)) {
+        if constexpr (kTight) {  // formed at each touch: no register held across the K loop
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            return pf_lane(el);
+        } else {
+            return pfoff;
         }
     };
 
     v4f acc[8][4];
+    // fragment addressing: rows 16k + frow share the swizzle of frow, so a
+    // lane's two piece offsets are fixed and subtiles step by 2 KiB
     const int frow = lane & 15;
     const int p0 = 2 * (lane >> 4);
     const int lo_off = frow * 128 + 16 * (p0 ^ swz(frow));
@@ -606,6 +349,16 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
         const uint4 hi = *reinterpret_cast<const uint4*>(base + hi_off);
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
+    // fp32 recipe: the partials of the subtile issued last and their scale
+    // factors, folded into the accumulators one subtile later (the last
+    // subtile of a K-block across the barrier into the next K-block), so that
+    // the matrix core has the next subtile's MFMAs to run while they wait.
+    // With 128x128 weight blocks the weights are the MFMA's 16-row operand
+    // and the tokens its 16 columns: a lane's four partials are then four
+    // weight rows of one token and share one factor sa[token] * sw[block],
+    // one multiply per subtile instead of one per row.  With per-row weight
+    // scales the tokens stay the row operand (each partial has its own
+    // factor either way, and this form holds fewer of them).
     v4f pend[4];
     float ps = 0.f;
     float psa[4] = {0.f, 0.f, 0.f, 0.f}, psw[4] = {0.f, 0.f, 0.f, 0.f};
@@ -649,9 +402,13 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
         }
     };
 
-    // The tile loop and its K loop, instantiated per wave role as in the tile
-    // kernel (waves 0-1 copy after the barrier, waves 2-3 before subtile
-    // kMidSubtile, waves 4-7 only compute).
+    // The tile loop and its K loop, instantiated per wave role so that no branch sits among the
+    // MFMAs: waves 0-1 copy their half of a stage right after the barrier
+    // (and issue the L2 prefetch), waves 2-3 after subtile kMidSubtile-1's
+    // MFMAs, waves 4-7 only compute.  Two half-size bursts on the DMA path
+    // hold each copying wave about half as long as one burst of all four.
+    // Not unrolled or peeled: a peeled first K-block is a second copy of the
+    // loop body, and that copy spills.
     auto run = [&](auto role) __attribute__((always_inline)) {
         constexpr int ROLE = decltype(role)::value;
         constexpr bool COPY = ROLE != kComputeOnly;
@@ -698,6 +455,8 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
                 issue(nx ? nab : q.ab, nx ? nwb : q.wb, nx ? nsab : q.sab, nx ? nswb : q.swb, k, (int)((kb + 1) & 1));
             };
             auto kblock = [&](int64_t kb) __attribute__((always_inline)) {
+                // this wave's copies of stage kb have landed (a prefetch issued
+                // after them may still be in flight: loads complete in order)
                 if constexpr (ROLE == kCopyTop) {
                     if (pf && kb > 0 && kb + p.pfd < p.KB) wait_vmcnt<1>();
                     else wait_vmcnt<0>();
@@ -709,7 +468,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
                 if constexpr (ROLE == kCopyTop) {
                     issue_next(kb);
                     if (pf && kb + 1 + p.pfd < p.KB)
-                        dma4s((wave == 0 ? q.ab : q.wb) + (kb + 1 + p.pfd) * 128, pfoff, sink);
+                        dma4s((wave == 0 ? q.ab : q.wb) + (kb + 1 + p.pfd) * 128, pf_off(), sink);
                 }
                 const uint8_t* st = ring[kb & 1];
                 const uint8_t* sta = st + TSA + 128 * wm * 128;
@@ -1288,13 +1047,6 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
         p.ntiles = (a.R + TBN - 1) / TBN;
         if (!set_tile_map(p, TNW * 64)) return hipErrorInvalidConfiguration;
         p.pfd = kTilePrefetch;
-        if (!a.mx && a.w_1x128) {
-            // fp32 scales with per-row weight scales: one tile per workgroup (the
-            // persistent form of this instantiation does not fit the register file)
-            hipLaunchKernelGGL((gemm_fp8_tile_kernel<false, true>), dim3(p.tpg * (uint32_t)p.G), dim3(TNW * 64), 0,
-                               stream, p);
-            return hipGetLastError();
-        }
         // persistent grid: at most one workgroup per CU, the same number on every XCD
         const uint32_t nblocks = p.tpg * (uint32_t)p.G;
         const DeviceInfo dev = current_device_info();
@@ -1314,7 +1066,10 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((gemm_fp8_ptile_kernel<true, false>), grid, dim3(TNW * 64), 0, stream, p);
         } else {
-            hipLaunchKernelGGL((gemm_fp8_ptile_kernel<false, false>), grid, dim3(TNW * 64), 0, stream, p);
+            if (a.w_1x128)
+                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<false, true>), grid, dim3(TNW * 64), 0, stream, p);
+            else
+                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<false, false>), grid, dim3(TNW * 64), 0, stream, p);
         }
     }
     return hipGetLastError();

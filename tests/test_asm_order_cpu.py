@@ -63,11 +63,9 @@ def test_one_launch_stores_are_complete_and_system_scope_before_the_arrival(asm)
 
 
 def test_plain_gemm_kernels_have_no_atomics(asm):
-    # the plain decode and tile kernels synchronise through LDS only (the
-    # persistent tile kernel: MX x per-row weight scales, and the fp32 recipe
-    # with 128x128 weight blocks; the one-tile-per-workgroup kernel: the fp32
-    # recipe with per-row weight scales)
-    for pattern, count in (("gemm_fp8_decode_kernel", 4), ("gemm_fp8_tile_kernel", 1), ("gemm_fp8_ptile_kernel", 3)):
+    # the plain decode and tile kernels synchronise through LDS only (both in
+    # their four instantiations: MX x per-row weight scales)
+    for pattern, count in (("gemm_fp8_decode_kernel", 4), ("gemm_fp8_ptile_kernel", 4)):
         fns = list(_functions(asm, pattern))
         assert len(fns) == count, pattern
         for name, lines in fns:
