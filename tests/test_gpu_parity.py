@@ -397,6 +397,37 @@ def test_grouped_gemm_persistent_tile_walks(T, G, hpg, R, brows, pow2):
     assert e <= TOL, e
 
 
+def _random_walks(n: int, seed: int):
+    """Seeded random shapes with more tiles than CUs (several tiles per
+    workgroup of the persistent tile kernel): ragged M and N tiles, every
+    scale recipe and weight-block layout."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(rng.integers(1500, 9001))
+        G = int(rng.integers(2, 17))
+        R = 64 * int(rng.integers(2, 17))
+        tiles = G * -(-T // 256) * -(-R // 256)
+        if tiles <= 256 or T * G * R > 40_000_000:
+            continue
+        out.append((T, G, int(rng.choice([1, 2])), R, int(rng.choice([1, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("T,G,hpg,R,brows,pow2", _random_walks(6, 2027))
+def test_grouped_gemm_random_persistent_walks(T, G, hpg, R, brows, pow2):
+    """Every output against the oracle's whole-tensor GEMM."""
+    w = wl.Workload(500 + T + G + R, "rwalk", T=T, n_groups=G, heads_per_group=hpg, o_lora_rank=R,
+                    max_pos=4096, positions="uniform", pow2=pow2, w_block_rows=brows)
+    o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
+    qr, sr = oracle.inv_rope_quant(o, pos, tab, G, hpg, pow2=pow2)
+    d_wq, d_ws, qwr, swr = _weights_both(w)
+    ref = oracle.grouped_gemm_full(qr, sr, qwr, swr, G, R, brows)
+    zg = gpu_gemm(w, qr, sr, d_wq, d_ws, brows, pow2)
+    e = U.rel_max_err(zg, ref)
+    assert e <= TOL, e
+
+
 def test_grouped_gemm_group_isolation_on_gpu():
     """Changing weight rows of other groups leaves a group's output unchanged."""
     w = wl.Workload(80, "iso", T=40, n_groups=3, heads_per_group=8, o_lora_rank=128, max_pos=4096,
