@@ -332,6 +332,7 @@ def test_grouped_gemm_pow2_padded_input():
 
 @pytest.mark.parametrize("T,G,R,brows,pow2", [(1, 2, 64, 128, False), (3, 1, 128, 1, False),
                                               (65, 2, 192, 128, False), (100, 3, 128, 1, True),
+                                              (128, 2, 320, 1, False), (128, 1, 64, 128, True),
                                               (129, 2, 128, 128, True), (300, 2, 320, 128, False),
                                               (513, 1, 256, 1, False)])
 def test_grouped_gemm_ragged(T, G, R, brows, pow2):
