@@ -1035,8 +1035,13 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     p.kbw = a.w_e8m0 ? p.KB / 4 : p.KB;
     p.e8 = a.a_e8m0;
     p.kshift = a.a_e8m0 ? 2 : 0;
-    // decode kernel for few tokens (the weight stream dominates), tile kernel otherwise
-    const bool decode = a.T <= 128;
+    // decode kernel for few tokens (the weight stream dominates), tile kernel
+    // otherwise.  Up to 256 tokens the tile kernel has a single M-tile per
+    // group, so at G=16, R=1024 it keeps 64 of 256 CUs busy (52-59 us for any
+    // T <= 256), while the decode kernel's 64-token M-tiles fill the chip
+    // (16.8 us at 64 tokens, 29 at 128, 44-45 at 160-192, 57 at 256); from
+    // 320 tokens on the tile kernel is ahead (55 vs 76 us).
+    const bool decode = a.T <= 256;
     if (decode) {
         p.mtiles = (a.T + DBM - 1) / DBM;
         p.ntiles = (a.R + DBN - 1) / DBN;

@@ -333,6 +333,7 @@ def test_grouped_gemm_pow2_padded_input():
 @pytest.mark.parametrize("T,G,R,brows,pow2", [(1, 2, 64, 128, False), (3, 1, 128, 1, False),
                                               (65, 2, 192, 128, False), (100, 3, 128, 1, True),
                                               (128, 2, 320, 1, False), (128, 1, 64, 128, True),
+                                              (160, 2, 192, 128, False), (256, 3, 320, 1, True),
                                               (129, 2, 128, 128, True), (300, 2, 320, 128, False),
                                               (513, 1, 256, 1, False)])
 def test_grouped_gemm_ragged(T, G, R, brows, pow2):
@@ -350,12 +351,12 @@ def test_grouped_gemm_ragged(T, G, R, brows, pow2):
 
 
 def _random_tile_shapes(n: int, seed: int):
-    """Seeded random shapes on the tile kernel (T > 128): ragged M- and N-tiles,
+    """Seeded random shapes on the tile kernel (T > 256): ragged M- and N-tiles,
     K-block counts 4 to 16, both weight-block layouts and both scale recipes."""
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
-        out.append((int(rng.integers(129, 601)), int(rng.integers(1, 4)), 64 * int(rng.integers(1, 6)),
+        out.append((int(rng.integers(257, 701)), int(rng.integers(1, 4)), 64 * int(rng.integers(1, 6)),
                     int(rng.choice([1, 2, 4])), int(rng.choice([1, 128])), bool(rng.integers(0, 2))))
     return out
 
