@@ -595,6 +595,13 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
 #endif
 constexpr int DBM = 64, DBN = 64, DNS = OPROJ_DEC_DNS, DKS = OPROJ_DEC_DKS;
 constexpr int DSTAGE = 64 * 128 * 2 + 512;  // activations + weights + scales
+// Token rows of a workgroup's tile: 64 * MM.  With MM = 2 (65-256 tokens)
+// the 128-token activation slab and the 64-row weight slab of a stage, with
+// their scales, take 24.75 KiB, so each K-group's ring holds 3 stages.
+template <int MM>
+constexpr int dstage() { return (64 * MM + DBN) * (128 + 4); }
+static_assert(dstage<1>() == DSTAGE, "one stage layout for 64-token tiles");
+constexpr int DNS2 = 3;  // ring stages with 128-token tiles
 constexpr int DVM = 9;  // one-launch path: copy instructions per copying wave per stage
 constexpr int DPROW = DBN + 4;  // fp32 per row of an epilogue partial tile (pad against bank conflicts)
 static_assert(DKS * DBM * DPROW * 4 <= DKS * DNS * DSTAGE, "the epilogue fits in the ring");
@@ -648,9 +655,15 @@ __device__ int group_barrier(uint64_t* sync, int64_t g, int64_t n, int spin) {
 // workgroup's LDS.  QCH > 0 is the one-launch path: the workgroup also
 // quantises its share of the group's activations (items of QCH heads, with
 // the rq::Params q) before the GEMM reads them.
-template <bool MX, bool W1, int QCH>
-__device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DKS][DNS][DSTAGE],
+template <bool MX, bool W1, int QCH, int MM = 1, int NS = DNS>
+__device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DKS][NS][dstage<MM>()],
                                             const rq::Params& q) {
+    static_assert(QCH == 0 || (MM == 1 && NS == DNS), "the one-launch path runs 64-token tiles");
+    constexpr int BM = 64 * MM;             // token rows of the tile
+    constexpr int STG = dstage<MM>();       // bytes per stage
+    constexpr int SWO = BM * 128;           // weight slab offset in a stage
+    constexpr int SCO = (BM + DBN) * 128;   // scale offset in a stage
+    static_assert(DKS * BM * DPROW * 4 <= DKS * NS * STG, "the epilogue fits in the ring");
     const int tid = threadIdx.x, lane = tid & 63;
     const int kq = __builtin_amdgcn_readfirstlane(tid >> 8);           // K-group
     const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // column group within the tile
@@ -659,14 +672,17 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // copies per K-block took about half of each step), waves 0-1 on the
     // one-launch path, whose prologue waits count that plan.
     constexpr int CW = QCH == 0 ? 4 : 2;
-    constexpr int CR = DBM / CW;  // rows of each slab per copying wave
-    constexpr int CI = CR / 8;    // copy instructions per slab per copying wave
+    constexpr int CR = DBN / CW;  // weight rows per copying wave
+    constexpr int CI = CR / 8;    // weight copy instructions per copying wave
+    constexpr int CRA = BM / CW;  // activation rows per copying wave
+    constexpr int CIA = CRA / 8;  // activation copy instructions per copying wave
     const bool copier = wave < CW;
-    const bool scaler = wave < 2;  // waves 0-1 also gather the scales
+    // scale gathers: waves 0-1 (64-token tiles), waves 0..MM (larger tiles)
+    const bool scaler = wave < (MM == 1 ? 2 : MM + 1);
     static_assert(QCH == 0 || 2 * CI + 1 == DVM, "the one-launch waits count DVM copies per step");
     const TileCoord tc = tile_coord(p);
     const int64_t g = tc.g, mt = tc.mt, nt = tc.nt;
-    const int64_t m0 = mt * DBM, n0 = nt * DBN;
+    const int64_t m0 = mt * BM, n0 = nt * DBN;
     // this K-group's K-blocks: [kb0, kb0 + nkb)
     const int64_t kb0 = p.KB * kq / DKS;
     const int64_t nkb = p.KB * (kq + 1) / DKS - kb0;
@@ -678,32 +694,39 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // uniform bases plus 32-bit lane offsets.
     const uint8_t* abase = p.a + g * p.sg;
     const uint8_t* wbase = p.w + g * p.R * p.D;
-    uint32_t off[2 * CI];
+    uint32_t off[CIA + CI];
     if (copier) {
 #pragma unroll
-        for (int j = 0; j < CI; ++j) {
-            const int row = CR * wave + 8 * j + (lane >> 3);
+        for (int j = 0; j < CIA; ++j) {
+            const int row = CRA * wave + 8 * j + (lane >> 3);
             const int piece = (lane & 7) ^ swz(row);
             int64_t m = m0 + row;
             m = m < p.T ? m : p.T - 1;  // rows past T are computed but never stored
             off[j] = (uint32_t)(m * p.st + piece * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < CI; ++j) {
+            const int row = CR * wave + 8 * j + (lane >> 3);
+            const int piece = (lane & 7) ^ swz(row);
             int64_t n = n0 + row;
             n = n < p.R ? n : p.R - 1;
-            off[CI + j] = (uint32_t)(n * p.D + piece * 16);
+            off[CIA + j] = (uint32_t)(n * p.D + piece * 16);
         }
     }
     // the scale gather mixes two sources across lanes: 64-bit lane addresses
+    // (larger tiles: wave c < MM gathers the activation scales of tokens
+    // 64c + l, wave MM the weight scales of the 64 columns)
     const float* ssrc;
     int64_t sstep;
     int kshl;  // K-blocks per scale word: activation words may pack four
-    if (lane < 32) {
-        int64_t m = m0 + 32 * (wave & 1) + lane;
+    if (MM > 1 ? wave < MM : lane < 32) {
+        int64_t m = m0 + (MM > 1 ? 64 * wave + lane : 32 * (wave & 1) + lane);
         m = m < p.T ? m : p.T - 1;
         ssrc = p.sa + m * p.sst + g * p.ssg;
         sstep = p.sskb;
         kshl = p.kshift;
     } else {
-        int64_t n = n0 + 32 * (wave & 1) + (lane - 32);
+        int64_t n = n0 + (MM > 1 ? lane : 32 * (wave & 1) + (lane - 32));
         n = n < p.R ? n : p.R - 1;
         ssrc = p.sw + wscale_index(p, g * p.R + n, 0);
         sstep = 1;
@@ -714,20 +737,20 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // instructions on waves 0-1, CI on the others), the weight slab (CI)
     auto issue_a = [&](int64_t i, int slot) __attribute__((always_inline)) {
         const int64_t kb = kb0 + i;
-        const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
+        const uint32_t st = ring0 + (uint32_t)(slot * STG);
 #pragma unroll
-        for (int j = 0; j < CI; ++j) dma16s(abase + kb * 128, off[j], st + (CR * wave + 8 * j) * 128);
-        if (scaler) dma4(ssrc + (kb >> kshl) * sstep, st + 16384 + 256 * wave);
+        for (int j = 0; j < CIA; ++j) dma16s(abase + kb * 128, off[j], st + (CRA * wave + 8 * j) * 128);
+        if (scaler) dma4(ssrc + (kb >> kshl) * sstep, st + SCO + 256 * wave);
     };
     auto issue_w = [&](int64_t i, int slot) __attribute__((always_inline)) {
         const int64_t kb = kb0 + i;
-        const uint32_t st = ring0 + (uint32_t)(slot * DSTAGE);
+        const uint32_t st = ring0 + (uint32_t)(slot * STG);
 #pragma unroll
         for (int j = 0; j < CI; ++j) {
             if (OPROJ_DEC_W_NT)
-                dma16s_nt(wbase + kb * 128, off[CI + j], st + 8192 + (CR * wave + 8 * j) * 128);
+                dma16s_nt(wbase + kb * 128, off[CIA + j], st + SWO + (CR * wave + 8 * j) * 128);
             else
-                dma16s(wbase + kb * 128, off[CI + j], st + 8192 + (CR * wave + 8 * j) * 128);
+                dma16s(wbase + kb * 128, off[CIA + j], st + SWO + (CR * wave + 8 * j) * 128);
         }
     };
     auto issue = [&](int64_t i, int slot) __attribute__((always_inline)) {
@@ -738,7 +761,7 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     if constexpr (QCH == 0) {
         if (copier) {
 #pragma unroll
-            for (int s = 0; s < DNS - 1; ++s)
+            for (int s = 0; s < NS - 1; ++s)
                 if (s < nkb) issue(s, s);
         }
     } else {
@@ -791,9 +814,11 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
         }
     }
 
-    v4f acc[4];
+    v4f acc[MM][4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) acc[mi] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int mi = 0; mi < MM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int frow = lane & 15;
     const int p0 = 2 * (lane >> 4);
@@ -812,46 +837,53 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
                 else if (i == 1) wait_vmcnt<5 * (DNS - 3) + DVM>();
                 else wait_vmcnt<5 * (DNS - 4 > 0 ? DNS - 4 : 0) + 2 * DVM>();
             } else if (scaler) {
-                wait_ahead<DNS - 2, 2 * CI + 1>(nkb - 1 - i);
+                wait_ahead<NS - 2, CIA + CI + 1>(nkb - 1 - i);
             } else {
-                wait_ahead<DNS - 2, 2 * CI>(nkb - 1 - i);
+                wait_ahead<NS - 2, CIA + CI>(nkb - 1 - i);
             }
         }
         __builtin_amdgcn_s_barrier();  // ... and every other wave's (no fence)
-        if (copier && i + DNS - 1 < nkb) issue(i + DNS - 1, (int)((i + DNS - 1) % DNS));
+        if (copier && i + NS - 1 < nkb) issue(i + NS - 1, (int)((i + NS - 1) % NS));
         if (i >= nkb) continue;        // uniform per wave group
-        const uint8_t* st = ring[kq][i % DNS];
-        // wave w: the 16 token rows 16w..16w+15 against all 64 columns (one
-        // activation fragment, four weight fragments per K-block)
-        const float* sc = reinterpret_cast<const float*>(st + 16384);
-        // scales: [64 * c + t] activation scale of token 32c + t, [64 * c + 32 + j]
-        // weight scale of column 32c + j (c = copying wave)
-        v8i af;
-        {
-            const int r = 16 * wave + frow;
+        const uint8_t* st = ring[kq][i % NS];
+        // wave w: the 16*MM token rows 16*MM*w.. against all 64 columns (MM
+        // activation fragments, four weight fragments per K-block)
+        const float* sc = reinterpret_cast<const float*>(st + SCO);
+        // scales, 64-token tiles: [64 * c + t] activation scale of token
+        // 32c + t, [64 * c + 32 + j] weight scale of column 32c + j (c =
+        // copying wave); larger tiles: [t] token t, [BM + j] column j
+        auto asc = [&](int r) __attribute__((always_inline)) { return MM > 1 ? r : 64 * (r >> 5) + (r & 31); };
+        auto wsc = [&](int n) __attribute__((always_inline)) { return MM > 1 ? BM + n : 64 * (n >> 5) + 32 + (n & 31); };
+        v8i af[MM];
+        float4 t4[MM];
+        int ea[MM];
+#pragma unroll
+        for (int mi = 0; mi < MM; ++mi) {
+            const int r = 16 * (MM * wave + mi) + frow;
             const uint4 lo = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * (p0 ^ swz(r)));
             const uint4 hi = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
-            af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const int r0 = 16 * (MM * wave + mi);  // this fragment's 16 token scales
+            if constexpr (MX) ea[mi] = act_e8m0(p, __float_as_uint(sc[asc(r0 + frow)]), kb0 + i);
+            else t4[mi] = *reinterpret_cast<const float4*>(sc + asc(r0 + 4 * (lane >> 4)));
         }
-        const float* sct = sc + 64 * (wave >> 1) + 16 * (wave & 1);  // this wave's 16 token scales
-        float4 t4;
-        int ea = 0;
-        if constexpr (MX) ea = act_e8m0(p, __float_as_uint(sct[frow]), kb0 + i);
-        else t4 = *reinterpret_cast<const float4*>(sct + 4 * (lane >> 4));
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
             const int r = 16 * ni + frow;
-            const uint4 lo = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * (p0 ^ swz(r)));
-            const uint4 hi = *reinterpret_cast<const uint4*>(st + 8192 + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + SWO + r * 128 + 16 * (p0 ^ swz(r)));
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + SWO + r * 128 + 16 * ((p0 + 1) ^ swz(r)));
             const v8i bfr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            const float swv = sc[64 * (ni >> 1) + 32 + 16 * (ni & 1) + (W1 || MX ? frow : 0)];
-            if constexpr (MX) {
-                acc[ni] = mfma_fp8_mx(af, bfr, acc[ni], ea, w_e8m0(p, __float_as_uint(swv), kb0 + i));
-            } else {
-                const float cmb[4] = {t4.x * swv, t4.y * swv, t4.z * swv, t4.w * swv};
-                const v4f pp = mfma_fp8(af, bfr, v4f{0.f, 0.f, 0.f, 0.f});
+            const float swv = sc[wsc(16 * ni + (W1 || MX ? frow : 0))];
 #pragma unroll
-                for (int i2 = 0; i2 < 4; ++i2) acc[ni][i2] = __builtin_fmaf(pp[i2], cmb[i2], acc[ni][i2]);
+            for (int mi = 0; mi < MM; ++mi) {
+                if constexpr (MX) {
+                    acc[mi][ni] = mfma_fp8_mx(af[mi], bfr, acc[mi][ni], ea[mi], w_e8m0(p, __float_as_uint(swv), kb0 + i));
+                } else {
+                    const float cmb[4] = {t4[mi].x * swv, t4[mi].y * swv, t4[mi].z * swv, t4[mi].w * swv};
+                    const v4f pp = mfma_fp8(af[mi], bfr, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) acc[mi][ni][i2] = __builtin_fmaf(pp[i2], cmb[i2], acc[mi][ni][i2]);
+                }
             }
         }
     }
@@ -861,21 +893,23 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     // ---- each K-group's fp32 partial tile into LDS (the ring is free now),
     // then every thread sums one 8-column chunk of one row over the K-groups
     // and writes it to z as bf16: whole 128-byte tile rows, 16-byte stores
-    float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [DKS][64][DPROW]
+    float* part = reinterpret_cast<float*>(&ring[0][0][0]);  // [DKS][BM][DPROW]
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int mi = 0; mi < MM; ++mi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            part[(kq * DBM + 16 * wave + 4 * (lane >> 4) + i) * DPROW + 16 * ni + frow] = acc[ni][i];
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                part[(kq * BM + 16 * (MM * wave + mi) + 4 * (lane >> 4) + i) * DPROW + 16 * ni + frow] = acc[mi][ni][i];
     __syncthreads();
-    for (int idx = tid; idx < DBM * (DBN / 8); idx += DKS * 256) {
+    for (int idx = tid; idx < BM * (DBN / 8); idx += DKS * 256) {
         const int r = idx / (DBN / 8), ch = idx % (DBN / 8);
         float4 s0 = *reinterpret_cast<const float4*>(part + r * DPROW + 8 * ch);
         float4 s1 = *reinterpret_cast<const float4*>(part + r * DPROW + 8 * ch + 4);
 #pragma unroll
         for (int q = 1; q < DKS; ++q) {
-            const float4 u0 = *reinterpret_cast<const float4*>(part + (q * DBM + r) * DPROW + 8 * ch);
-            const float4 u1 = *reinterpret_cast<const float4*>(part + (q * DBM + r) * DPROW + 8 * ch + 4);
+            const float4 u0 = *reinterpret_cast<const float4*>(part + (q * BM + r) * DPROW + 8 * ch);
+            const float4 u1 = *reinterpret_cast<const float4*>(part + (q * BM + r) * DPROW + 8 * ch + 4);
             s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
             s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
         }
@@ -888,11 +922,12 @@ __device__ __forceinline__ void decode_tile(const GParams& p, uint8_t (&ring)[DK
     }
 }
 
-template <bool MX, bool W1>
+template <bool MX, bool W1, int MM>
 __global__ __launch_bounds__(DKS * 256) void gemm_fp8_decode_kernel(GParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][DNS][DSTAGE];
+    constexpr int NS = MM == 1 ? DNS : DNS2;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[DKS][NS][dstage<MM>()];
     const rq::Params none{};
-    decode_tile<MX, W1, 0>(p, ring, none);
+    decode_tile<MX, W1, 0, MM, NS>(p, ring, none);
 }
 
 // One launch for a decode step: quantisation (spread over the GEMM's own
@@ -921,18 +956,19 @@ bool set_tile_map(GParams& p, int threads) {
     return true;
 }
 
+template <int MM>
 void launch_decode(const GParams& p, bool mx, bool w1, hipStream_t stream) {
     const dim3 grid(p.tpg * (uint32_t)p.G), block(DKS * 256);
     if (mx) {
         if (w1)
-            hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, true, MM>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<true, false, MM>), grid, block, 0, stream, p);
     } else {
         if (w1)
-            hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, true, MM>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_fp8_decode_kernel<false, false, MM>), grid, block, 0, stream, p);
     }
 }
 
@@ -1038,15 +1074,21 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
     // decode kernel for few tokens (the weight stream dominates), tile kernel
     // otherwise.  Up to 256 tokens the tile kernel has a single M-tile per
     // group, so at G=16, R=1024 it keeps 64 of 256 CUs busy (52-59 us for any
-    // T <= 256), while the decode kernel's 64-token M-tiles fill the chip
-    // (16.8 us at 64 tokens, 29 at 128, 44-45 at 160-192, 57 at 256); from
-    // 320 tokens on the tile kernel is ahead (55 vs 76 us).
+    // T <= 256), while the decode kernel's tiles fill the chip (17-18 us at
+    // 64 tokens, 22 at 96-128, 40-43 at 160-256); from 320 tokens on the
+    // tile kernel is ahead (55 vs 63 us).
     const bool decode = a.T <= 256;
     if (decode) {
-        p.mtiles = (a.T + DBM - 1) / DBM;
+        // 64-token tiles up to 64 tokens, 128-token tiles above (one weight
+        // stream per 128 tokens instead of two)
+        const int bm = a.T <= DBM ? DBM : 2 * DBM;
+        p.mtiles = (a.T + bm - 1) / bm;
         p.ntiles = (a.R + DBN - 1) / DBN;
         if (!set_tile_map(p, DKS * 256)) return hipErrorInvalidConfiguration;
-        launch_decode(p, a.mx != 0, a.w_1x128 != 0, stream);
+        if (bm == DBM)
+            launch_decode<1>(p, a.mx != 0, a.w_1x128 != 0, stream);
+        else
+            launch_decode<2>(p, a.mx != 0, a.w_1x128 != 0, stream);
     } else {
         p.mtiles = (a.T + TBM - 1) / TBM;
         p.ntiles = (a.R + TBN - 1) / TBN;
