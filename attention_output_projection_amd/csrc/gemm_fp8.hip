@@ -130,7 +130,8 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 // Tile kernel (large T): 256x256 output tiles, one 512-thread workgroup per
 // CU walking a sequence of tiles (below), eight waves as 2 (M) x 4 (N) of
 // 128x64 (32 MFMAs per K-block per wave, 128 fp32 accumulators in VGPRs),
-// two waves per SIMD.  The tile and wave shapes keep
+// two waves per SIMD.  (Batches whose 256-row tiles would leave half the CUs
+// idle take 128x256 tiles instead: waves of 64x64, the same pipeline.)  The tile and wave shapes keep
 // LDS reads per MFMA low: per K-block the workgroup reads 192 KiB of
 // fragments and copies 64 KiB for 2048 MFMA cycles per SIMD.  Each K-block is
 // one pipeline stage (256x128-byte activation slab, 256x128-byte weight slab,
@@ -161,8 +162,13 @@ __device__ __forceinline__ int w_e8m0(const GParams& p, uint32_t raw, int64_t kb
 // one subtile later (the last subtile of a K-block after the next barrier),
 // so the matrix core runs the next MFMAs while the promotion waits for them.
 constexpr int TBM = 256, TBN = 256, TNS = 2, TNW = 8;
-constexpr int TSA = 0, TSB = TBM * 128, TSS = TSB + TBN * 128, TSW = TSS + 1024;
-constexpr int TSTAGE = TSW + 1024;  // 67584 bytes
+// Stage layout for tiles of bm rows (256, or 128 when 256-row tiles would
+// leave CUs idle): activation slab, weight slab, 256 activation scale slots
+// (64 per copying wave), 256 weight scales.
+constexpr int tsb(int bm) { return bm * 128; }
+constexpr int tss(int bm) { return tsb(bm) + TBN * 128; }
+constexpr int tsw(int bm) { return tss(bm) + 1024; }
+constexpr int tstage(int bm) { return tsw(bm) + 1024; }  // 67584 bytes at 256 rows
 constexpr int kTilePrefetch = 2;    // L2 prefetch distance in K-blocks (measured best of 2, 3, 4, 6)
 constexpr int kCopyTop = 0, kCopyMid = 1, kComputeOnly = 2;  // wave roles in the K loop
 constexpr int kMidSubtile = 4;  // waves 2-3 copy before this subtile's MFMAs (2, 3, 4 measured alike; 6 slower)
@@ -216,17 +222,17 @@ struct TilePlan {
     int64_t g, m0, n0;
     bool full;
 };
-template <typename PP>
+template <int BM, typename PP>
 __device__ __forceinline__ TilePlan tile_plan(const PP& p, uint32_t t) {
     const uint32_t g = t / p.tpg, r = t - g * p.tpg, mt = r / p.nt32, nt = r - mt * p.nt32;
     TilePlan q;
     q.g = g;
     q.mt = (int32_t)mt;
     q.nt = (int32_t)nt;
-    q.m0 = (int64_t)mt * TBM;
+    q.m0 = (int64_t)mt * BM;
     q.n0 = (int64_t)nt * TBN;
     const int64_t ml = p.T - 1 - q.m0, nl = p.R - 1 - q.n0;
-    q.mlim = (int32_t)(ml < TBM ? ml : TBM);
+    q.mlim = (int32_t)(ml < BM ? ml : BM);
     q.nlim = (int32_t)(nl < TBN ? nl : TBN);
     const int64_t wrow = (int64_t)g * p.R + q.n0;
     q.wphase = (int32_t)(wrow & ((1 << p.w_shift) - 1));
@@ -234,7 +240,7 @@ __device__ __forceinline__ TilePlan tile_plan(const PP& p, uint32_t t) {
     q.wb = p.w + wrow * p.D;
     q.sab = reinterpret_cast<const uint8_t*>(p.sa + (int64_t)g * p.ssg + q.m0 * p.sst);
     q.swb = reinterpret_cast<const uint8_t*>(p.sw + (wrow >> p.w_shift) * p.kbw);
-    q.full = q.mlim >= TBM - 1 && q.nlim >= TBN - 1;
+    q.full = q.mlim >= BM - 1 && q.nlim >= TBN - 1;
     return q;
 }
 
@@ -250,9 +256,17 @@ __device__ __forceinline__ KGParams& params_reloaded() {
     return *reinterpret_cast<KGParams*>(v);
 }
 
-template <bool MX, bool W1>
+// MS: 16-row M-subtiles per wave; the tile has 32 * MS rows (8: 256 rows, 4:
+// 128 rows, for batches whose 256-row tiles would not fill the CUs).
+template <bool MX, bool W1, int MS>
 __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
-    constexpr bool kTight = W1 && !MX;  // the instantiation with the most live registers
+    constexpr bool kTight = W1 && !MX && MS == 8;  // the instantiation with the most live registers
+    constexpr int BM = 32 * MS;                     // tile rows
+    constexpr int CRA = BM / 4;                     // activation rows per copying wave
+    constexpr int TSB = tsb(BM), TSS = tss(BM), TSW = tsw(BM), TSTAGE = tstage(BM);
+    constexpr int MID = MS == 8 ? kMidSubtile : MS / 2;  // the mid copiers' subtile
+    // activation scale slot of tile row r: 64 slots per copying wave, CRA used
+    auto asl = [](int r) __attribute__((always_inline)) { return MS == 8 ? r : 64 * (r / CRA) + r % CRA; };
     __shared__ __attribute__((aligned(1024))) uint8_t ring[TNS][TSTAGE];
     __shared__ __attribute__((aligned(16))) uint16_t epi[TNW][16 * PEROW];
     __shared__ __attribute__((aligned(256))) uint8_t pf_sink[256];
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
     // weight rows 64c..64c+63 of the tile (8 rows of 128 bytes per
     // instruction) and the scales of those rows; lane offsets relative to the
     // tile's scalar bases, rows clamped to the tile's last valid row.
-    uint32_t off[16], soffa = 0, soffw = 0;
+    uint32_t off[MS + 8], soffa = 0, soffw = 0;
     auto plan_lanes = [&](KGParams& pr, const TilePlan& q) __attribute__((always_inline)) {
         if (copier) {
             // fp32 with per-row weight scales (the instantiation with the most
@@ -276,28 +290,35 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
             int el = lane;
             if constexpr (kTight) asm volatile("" : "+v"(el));
 #pragma unroll
+            for (int j = 0; j < MS; ++j) {
+                const int row = CRA * wave + 8 * j + (el >> 3);
+                const uint32_t piece = (uint32_t)(((el & 7) ^ swz(row)) * 16);
+                off[j] = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.st + piece;
+            }
+#pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int row = 64 * wave + 8 * j + (el >> 3);
                 const uint32_t piece = (uint32_t)(((el & 7) ^ swz(row)) * 16);
-                off[j] = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.st + piece;
-                off[8 + j] = (uint32_t)(row < q.nlim ? row : q.nlim) * (uint32_t)pr.D + piece;
+                off[MS + j] = (uint32_t)(row < q.nlim ? row : q.nlim) * (uint32_t)pr.D + piece;
             }
+            // (128-row tiles: lanes 32-63 repeat lanes 0-31 into unused slots)
+            const int arow = CRA * wave + (MS == 8 ? el : (el & 31));
+            soffa = (uint32_t)(arow < q.mlim ? arow : q.mlim) * (uint32_t)pr.sst * 4u;
             const int row = 64 * wave + el;
-            soffa = (uint32_t)(row < q.mlim ? row : q.mlim) * (uint32_t)pr.sst * 4u;
             soffw = (uint32_t)(((q.wphase + (row < q.nlim ? row : q.nlim)) >> pr.w_shift) * pr.kbw) * 4u;
         }
     };
     const uint32_t ring0 = lds_offset(&ring[0][0]);
-    const uint32_t adst = ring0 + TSA + 64 * (wave & 3) * 128, wdst = ring0 + TSB + 64 * (wave & 3) * 128;
+    const uint32_t adst = ring0 + CRA * (wave & 3) * 128, wdst = ring0 + TSB + 64 * (wave & 3) * 128;
     auto issue = [&](const uint8_t* ab, const uint8_t* wb, const uint8_t* sab, const uint8_t* swb, int64_t kb,
                      int slot) __attribute__((always_inline)) {
         const uint32_t so = (uint32_t)(slot * TSTAGE);
         ab += kb * 128;
         wb += kb * 128;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dma16s(ab, off[j], adst + so + j * 1024);
+        for (int j = 0; j < MS; ++j) dma16s(ab, off[j], adst + so + j * 1024);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dma16s(wb, off[8 + j], wdst + so + j * 1024);
+        for (int j = 0; j < 8; ++j) dma16s(wb, off[MS + j], wdst + so + j * 1024);
         dma4s(sab + (kb >> p.kshift) * p.sskb * 4, soffa, ring0 + so + TSS + 256 * (wave & 3));
         dma4s(swb + (kb >> p.wkshift) * 4, soffw, ring0 + so + TSW + 256 * (wave & 3));
     };
@@ -312,12 +333,12 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
     int32_t pf_row0 = 0, pf_lim = 0;
     uint32_t pf_stride = 0, pfoff = 0;
     auto pf_lane = [&](int el) __attribute__((always_inline)) {
-        const int row = pf_row0 + (wave == 0 ? el : (el & 31));
+        const int row = pf_row0 + (wave == 0 && MS == 8 ? el : (el & 31));
         return (uint32_t)(row < pf_lim ? row : pf_lim) * pf_stride;
     };
     auto plan_pf = [&](KGParams& pr, const TilePlan& q) __attribute__((always_inline)) {
         if (wave == 0) {
-            pf_row0 = 64 * q.nt;
+            pf_row0 = (BM / 4) * q.nt;
             pf_lim = q.mlim;
             pf_stride = (uint32_t)pr.st;
         } else if (wave == 1) {
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
         }
     };
 
-    v4f acc[8][4];
+    v4f acc[MS][4];
     // fragment addressing: rows 16k + frow share the swizzle of frow, so a
     // lane's two piece offsets are fixed and subtiles step by 2 KiB
     const int frow = lane & 15;
@@ -414,7 +435,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
         constexpr bool COPY = ROLE != kComputeOnly;
         bool first = true, chained = false;
         for (uint32_t i = seq.first; i < seq.limit; i += seq.step) {
-            const TilePlan q = tile_plan(params_reloaded(), seq.base + i);
+            const TilePlan q = tile_plan<BM>(params_reloaded(), seq.base + i);
             if constexpr (COPY) {
                 plan_lanes(params_reloaded(), q);
                 if (!chained) {
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
             const uint8_t *nab = q.ab, *nwb = q.wb, *nsab = q.sab, *nswb = q.swb;
             bool chain = false;
             if (has_next && p.xnext && q.full) {
-                const TilePlan qn = tile_plan(params_reloaded(), seq.base + inext);
+                const TilePlan qn = tile_plan<BM>(params_reloaded(), seq.base + inext);
                 chain = qn.full;
                 nab = qn.ab;
                 nwb = qn.wb;
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
             chained = chain;
             const bool pf = p.pfd > 0 && ROLE == kCopyTop && (wave == 1 || q.nt < 4);
 #pragma unroll
-            for (int mi = 0; mi < 8; ++mi)
+            for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -471,7 +492,7 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
                         dma4s((wave == 0 ? q.ab : q.wb) + (kb + 1 + p.pfd) * 128, pf_off(), sink);
                 }
                 const uint8_t* st = ring[kb & 1];
-                const uint8_t* sta = st + TSA + 128 * wm * 128;
+                const uint8_t* sta = st + (BM / 2) * wm * 128;
                 const uint8_t* stb = st + TSB + 64 * wn * 128;
                 const float* sca = reinterpret_cast<const float*>(st + TSS);
                 const float* scw = reinterpret_cast<const float*>(st + TSW);
@@ -484,17 +505,17 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni)
                         eb[ni] = w_e8m0(p, __float_as_uint(scw[64 * wn + 16 * ni + frow]), kb);
-                    float san = sca[128 * wm + frow];
+                    float san = sca[asl((BM / 2) * wm + frow)];
 #pragma unroll
-                    for (int mi = 0; mi < 8; ++mi) {
+                    for (int mi = 0; mi < MS; ++mi) {
                         if constexpr (ROLE == kCopyMid) {
-                            if (mi == kMidSubtile) issue_next(kb);
+                            if (mi == MID) issue_next(kb);
                         }
                         const v8i af = afn;
                         const int ea = act_e8m0(p, __float_as_uint(san), kb);
-                        if (mi < 7) {
+                        if (mi < MS - 1) {
                             afn = frag(sta + (mi + 1) * 2048);
-                            san = sca[128 * wm + 16 * (mi + 1) + frow];
+                            san = sca[asl((BM / 2) * wm + 16 * (mi + 1) + frow)];
                         }
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni)
@@ -504,23 +525,27 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
                     float swv[4];
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni) swv[ni] = scw[64 * wn + 16 * ni + frow];
-                    const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * (128 * wm + 4 * (lane >> 4));
+                    // this lane's first token row (128-row tiles: its scale slot per subtile)
+                    const int tr = (BM / 2) * wm + 4 * (lane >> 4);
+                    const uint8_t* sab = reinterpret_cast<const uint8_t*>(sca) + 4 * asl(tr);
                     float4 tn = *reinterpret_cast<const float4*>(sab);
 #pragma unroll
-                    for (int mi = 0; mi < 8; ++mi) {
+                    for (int mi = 0; mi < MS; ++mi) {
                         if constexpr (ROLE == kCopyMid) {
-                            if (mi == kMidSubtile) issue_next(kb);
+                            if (mi == MID) issue_next(kb);
                         }
                         const v8i af = afn;
                         const float sa4[4] = {tn.x, tn.y, tn.z, tn.w};
-                        if (mi < 7) {
+                        if (mi < MS - 1) {
                             afn = frag(sta + (mi + 1) * 2048);
-                            tn = *reinterpret_cast<const float4*>(sab + 64 * (mi + 1));
+                            tn = *reinterpret_cast<const float4*>(
+                                MS == 8 ? sab + 64 * (mi + 1)
+                                        : reinterpret_cast<const uint8_t*>(sca + asl(tr + 16 * (mi + 1))));
                         }
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni) {
                             const v4f qv = mfma_fp8(af, bfr[ni], v4f{0.f, 0.f, 0.f, 0.f});
-                            fold(mi == 0 ? 7 : mi - 1, ni);
+                            fold(mi == 0 ? MS - 1 : mi - 1, ni);
                             pend[ni] = qv;
                             if (mi == 0) psw[ni] = swv[ni];
                         }
@@ -529,22 +554,22 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
                     }
                 } else {
                     const float sws = scw[64 * wn];
-                    float san = sca[128 * wm + frow];
+                    float san = sca[asl((BM / 2) * wm + frow)];
 #pragma unroll
-                    for (int mi = 0; mi < 8; ++mi) {
+                    for (int mi = 0; mi < MS; ++mi) {
                         if constexpr (ROLE == kCopyMid) {
-                            if (mi == kMidSubtile) issue_next(kb);
+                            if (mi == MID) issue_next(kb);
                         }
                         const v8i af = afn;
                         const float sa = san;
-                        if (mi < 7) {
+                        if (mi < MS - 1) {
                             afn = frag(sta + (mi + 1) * 2048);
-                            san = sca[128 * wm + 16 * (mi + 1) + frow];
+                            san = sca[asl((BM / 2) * wm + 16 * (mi + 1) + frow)];
                         }
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni) {
                             const v4f qv = mfma_fp8(bfr[ni], af, v4f{0.f, 0.f, 0.f, 0.f});
-                            fold(mi == 0 ? 7 : mi - 1, ni);
+                            fold(mi == 0 ? MS - 1 : mi - 1, ni);
                             pend[ni] = qv;
                         }
                         ps = sa * sws;
@@ -555,14 +580,14 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
             for (int64_t kb = 0; kb < p.KB; ++kb) kblock(kb);
             if constexpr (!MX) {
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) fold(7, ni);
+                for (int ni = 0; ni < 4; ++ni) fold(MS - 1, ni);
             }
             // this wave's results to z, subtile by subtile
             KGParams& pr = params_reloaded();
-            const int64_t r0 = q.m0 + 128 * wm, c0 = q.n0 + 64 * wn, zrs = pr.G * pr.R;
+            const int64_t r0 = q.m0 + (BM / 2) * wm, c0 = q.n0 + 64 * wn, zrs = pr.G * pr.R;
             uint16_t* zb = pr.z + r0 * zrs + q.g * pr.R + c0;
 #pragma unroll
-            for (int mi = 0; mi < 8; ++mi) store_sub(mi, zb, zrs, pr.T - r0, pr.R - c0);
+            for (int mi = 0; mi < MS; ++mi) store_sub(mi, zb, zrs, pr.T - r0, pr.R - c0);
         }
     };
     if (wave < 2) run(std::integral_constant<int, kCopyTop>{});
@@ -1090,13 +1115,22 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
         else
             launch_decode<2>(p, a.mx != 0, a.w_1x128 != 0, stream);
     } else {
-        p.mtiles = (a.T + TBM - 1) / TBM;
-        p.ntiles = (a.R + TBN - 1) / TBN;
+        // 256-row tiles, or 128-row tiles when 256-row tiles would leave at
+        // least half the CUs idle and 128-row tiles still fit in one round.
+        // A 128-row tile costs 62-64% of a 256-row one (its copies per MFMA
+        // are 1.5x), so only then do they pay: G=16, R=1024, 288-512 tokens
+        // 46.8-49.8 against 55.8-60.3 us; at 640-1024 tokens (a second round
+        // of 128-row tiles) 80-90 against 60-72 us.
+        const DeviceInfo dev = current_device_info();
+        const int64_t nt = (a.R + TBN - 1) / TBN;
+        const int64_t t256 = a.G * ((a.T + 255) / 256) * nt, t128 = a.G * ((a.T + 127) / 128) * nt;
+        const int bm = 2 * t256 <= dev.cus && t128 <= dev.cus ? 128 : 256;
+        p.mtiles = (a.T + bm - 1) / bm;
+        p.ntiles = nt;
         if (!set_tile_map(p, TNW * 64)) return hipErrorInvalidConfiguration;
         p.pfd = kTilePrefetch;
         // persistent grid: at most one workgroup per CU, the same number on every XCD
         const uint32_t nblocks = p.tpg * (uint32_t)p.G;
-        const DeviceInfo dev = current_device_info();
         uint32_t wgs;
         if (p.xcd_per) {
             const uint32_t per = (uint32_t)(dev.cus >> p.xcd_shift);
@@ -1106,18 +1140,16 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, hipStream_t stream) {
         }
         p.ntot = nblocks;
         p.xnext = a.R % TBN == 0;
-        const dim3 grid(wgs);
+        const dim3 grid(wgs), block(TNW * 64);
+#define OPROJ_PTILE(MXV, W1V)                                                                      \
+    if (bm == 256) hipLaunchKernelGGL((gemm_fp8_ptile_kernel<MXV, W1V, 8>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((gemm_fp8_ptile_kernel<MXV, W1V, 4>), grid, block, 0, stream, p)
         if (a.mx) {
-            if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<true, true>), grid, dim3(TNW * 64), 0, stream, p);
-            else
-                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<true, false>), grid, dim3(TNW * 64), 0, stream, p);
+            if (a.w_1x128) { OPROJ_PTILE(true, true); } else { OPROJ_PTILE(true, false); }
         } else {
-            if (a.w_1x128)
-                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<false, true>), grid, dim3(TNW * 64), 0, stream, p);
-            else
-                hipLaunchKernelGGL((gemm_fp8_ptile_kernel<false, false>), grid, dim3(TNW * 64), 0, stream, p);
+            if (a.w_1x128) { OPROJ_PTILE(false, true); } else { OPROJ_PTILE(false, false); }
         }
+#undef OPROJ_PTILE
     }
     return hipGetLastError();
 }

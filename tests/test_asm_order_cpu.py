@@ -63,10 +63,10 @@ def test_one_launch_stores_are_complete_and_system_scope_before_the_arrival(asm)
 
 
 def test_plain_gemm_kernels_have_no_atomics(asm):
-    # the plain decode and tile kernels synchronise through LDS only (the tile
-    # kernel in its four instantiations, MX x per-row weight scales, the
-    # decode kernel in those four for each of its 64- and 128-token tiles)
-    for pattern, count in (("gemm_fp8_decode_kernel", 8), ("gemm_fp8_ptile_kernel", 4)):
+    # the plain decode and tile kernels synchronise through LDS only (both in
+    # their four instantiations, MX x per-row weight scales, for each of
+    # their two tile heights)
+    for pattern, count in (("gemm_fp8_decode_kernel", 8), ("gemm_fp8_ptile_kernel", 8)):
         fns = list(_functions(asm, pattern))
         assert len(fns) == count, pattern
         for name, lines in fns:
