@@ -825,13 +825,14 @@ def test_grouped_gemm_every_output_full_size(name):
 
 
 @pytest.mark.parametrize("T,G,pow2,brows", [(512, 16, False, 128), (513, 16, False, 128), (1000, 8, True, 1),
-                                             (384, 16, True, 1)])
+                                             (384, 16, True, 1), (200, 16, False, 128), (128, 16, True, 1)])
 def test_grouped_gemm_every_output_both_tile_heights(T, G, pow2, brows):
-    """Every z around the tile kernel's choice of tile height at 16 and 8
-    groups of 1024 columns: 512 tokens (16 groups) and 1000 tokens (8 groups)
+    """Every z around the kernels' choice of tile at 16 and 8 groups of 1024
+    columns.  Tile kernel: 512 tokens (16 groups) and 1000 tokens (8 groups)
     run 256 tiles of 128 rows, one per CU, in the XCD tile order; 513 tokens
-    runs 192 tiles of 256 rows; 384 tokens 192 tiles of 128 rows.  Both scale
-    recipes, against the oracle chain."""
+    runs 192 tiles of 256 rows; 384 tokens 192 tiles of 128 rows.  Decode
+    kernel with 128-token tiles: 200 tokens in two rounds of 256 workgroups,
+    128 tokens in one.  Both scale recipes, against the oracle chain."""
     w = wl.Workload(900 + T, "heights", T=T, n_groups=G, heads_per_group=8, o_lora_rank=1024, max_pos=8192,
                     positions="uniform", pow2=pow2, w_block_rows=brows)
     o, pos, tab = wl.attn_out(w), wl.positions(w), wl.table(w)
