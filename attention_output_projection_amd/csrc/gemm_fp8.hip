@@ -598,18 +598,21 @@ __global__ __launch_bounds__(TNW * 64) void gemm_fp8_ptile_kernel(GParams p) {
 
 // ---------------------------------------------------------------------------
 // Decode kernel (few tokens): the weight stream is the cost.
-// Workgroup tile: one group, 64 tokens x 64 columns, the whole K.  Each
-// K-block is one pipeline stage in LDS: the 64x128-byte activation slab, the
-// 64x128-byte weight slab and the block's scales, all copied by the DMA form
+// Workgroup tile: one group, 64 tokens (128 above 64 tokens) x 64 columns,
+// the whole K.  Each K-block is one pipeline stage in LDS: the 64x128-byte
+// (128x128-byte) activation slab, the 64x128-byte weight slab and the
+// block's scales, all copied by the DMA form
 // of the global loads (global_load_lds: no staging registers).  The eight
 // waves form DKS K-groups of four; each K-group walks its share of the
-// K-blocks through its own ring of DNS stages, DNS-1 of them in flight, with
+// K-blocks through its own ring of DNS stages (DNS2 with 128-token tiles),
+// all but one of them in flight, with
 // one s_waitcnt + barrier per K-block.  Every wave of a K-group issues a
 // quarter of the copies (the one-launch path: waves 0-1 half each).  Rows
 // are 128 bytes with the 16-byte pieces XOR-swizzled, which makes the
 // fragment reads conflict-free.  For the MFMAs
-// the waves of a K-group split M: wave w owns token rows 16w..16w+15 against
-// all 64 columns (one activation and four weight fragments per K-block, a
+// the waves of a K-group split M: wave w owns token rows 16w..16w+15 (32w..
+// 32w+31 with 128-token tiles) against all 64 columns (one or two activation
+// fragments and four weight fragments per K-block, a
 // third less LDS reading than splitting N); the K-groups' partial tiles are
 // summed through LDS and written as whole 128-byte rows of z.
 #ifndef OPROJ_DEC_DNS
